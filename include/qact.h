@@ -1,0 +1,203 @@
+/*
+ * qact.h - C ABI of the MI355X (gfx950) quantized-linear library libqact.so.
+ *
+ * The operations are those of 6Bit-Diffusion (arXiv 2603.18742): each
+ * internal linear layer of a video-DiT block quantizes its activations at
+ * inference time to NVFP4 or INT8, chosen per layer (abstract; Fig. 2
+ * caption), and multiplies them with 4-bit NVFP4 weights (Table 2, "W4");
+ * the choice comes from a linear predictor on the block's input/output
+ * relative L1 distance Gamma at the preceding timestep (Fig. 3 caption);
+ * the Temporal Delta Cache stores a block's residual Delta = out - in and
+ * reuses it when the two preceding Deltas agree (abstract; Fig. 2 and
+ * Fig. 4 captions).
+ *
+ * Formats (the pages name NVFP4 and INT8 and print no rounding rules; the
+ * readings below hold throughout):
+ *   NVFP4  codes  u8 [rows][K/2]: E2M1 element 2j in the low nibble, 2j+1
+ *                 in the high nibble; bit 3 of a nibble is the sign.
+ *          scales u8 [rows][K/16]: one OCP E4M3FN scale per 16 elements.
+ *          tscale f32 scalar: the tensor scale s_T.
+ *          Encode (float32, in order; recip(y) = y == 0 ? 0 : 1/y):
+ *            s_T = amax/2688; g = recip(6 s_T); enc = E4M3(amax_group * g);
+ *            inv = recip(E4M3value(enc) * s_T); code = E2M1(x * inv).
+ *          E2M1 and E4M3 round to nearest, ties to the even code, and
+ *          saturate (6 and 448); a negative x that rounds to 0 keeps its
+ *          sign bit.  K must be a multiple of 16.
+ *   INT8   q i8 [rows][K], scale f32 [rows], per token (row), symmetric:
+ *          s = amax_row/127, inv = recip(s), q = clamp(rint(x*inv), +-127).
+ *   bf16   uint16 bit patterns; tensors are row-major.
+ *
+ * Conventions for every device entry point:
+ *   - tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing; ``ws``/``ws_bytes`` is caller-owned device scratch
+ *     of at least the size the matching *_workspace() call returns;
+ *   - arguments are validated on the host first; when a call returns an
+ *     error, nothing was enqueued;
+ *   - work is enqueued on ``stream`` and the call returns without waiting;
+ *     device faults surface at the caller's next synchronisation;
+ *   - vector buffers must be 16-byte aligned; row strides are in elements;
+ *   - results are deterministic: no floating-point atomics anywhere;
+ *   - calls on different streams must not share output or scratch buffers.
+ */
+#ifndef QACT_H
+#define QACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QA_OK = 0,
+  QA_EINVAL = -1,        /* null pointer, bad enum, negative size         */
+  QA_ESHAPE = -2,        /* K % 16 != 0, ld < K, sizes beyond the limits  */
+  QA_EALIGN = -3,        /* a vector buffer is not 16-byte aligned        */
+  QA_EUNSUPPORTED = -4,  /* a valid but unimplemented combination         */
+  QA_EWORKSPACE = -5,    /* ws_bytes below the required size              */
+  QA_EHIP = -6,          /* a HIP launch failed                           */
+  QA_EALIAS = -7         /* an output overlaps an input it must not alias */
+} qa_status;
+
+typedef enum { QA_NVFP4 = 0, QA_INT8 = 1 } qa_fmt;
+typedef enum { QA_OUT_BF16 = 0, QA_OUT_F32 = 1 } qa_out;
+typedef enum { QA_EPI_NONE = 0, QA_EPI_GELU_TANH = 1 } qa_epi;
+
+/* NVFP4 only: *tscale is an input (a calibrated or producer-computed s_T)
+ * and the tensor amax pass is skipped. */
+#define QA_TSCALE_GIVEN 1u
+
+/* Human-readable name of a status code (static storage). */
+const char* qa_strerror(int status);
+
+/* Library version and the GPU architecture the kernels were built for. */
+const char* qa_build_info(void);
+
+/* ------------------------------------------------------------------------
+ * Activation (and weight) quantization.  Abstract: activations are
+ * quantized on the fly to NVFP4 or INT8; Fig. 2 caption: the bits are per
+ * linear layer.  Weights use the same NVFP4 call once at set-up.
+ *
+ * x      bf16 [M][ldx] (first K columns used), 16-byte aligned, ldx % 8 == 0
+ * q      NVFP4: u8 [M][K/2];  INT8: i8 [M][K]
+ * scales NVFP4: u8 [M][K/16];  INT8: f32 [M]
+ * tscale NVFP4: f32 device scalar, output (or input with QA_TSCALE_GIVEN);
+ *        INT8: must be NULL
+ * M >= 0 (M == 0 enqueues nothing), 0 < K, K % 16 == 0 for NVFP4.
+ * ------------------------------------------------------------------------ */
+size_t act_quant_workspace(qa_fmt fmt, int64_t M, int64_t K);
+int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+              void* q, void* scales, float* tscale, uint32_t flags,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Quantized linear  Y[M][N] = dequant(A) dequant(W)^T (+ bias) (-> GELU).
+ * Abstract and Fig. 2: each internal linear runs on NVFP4 or INT8
+ * activations against 4-bit (NVFP4) weights.
+ *
+ * A NVFP4 (a_q, a_s, a_ts) or INT8 (a_q, a_s) as produced by act_quant;
+ * W NVFP4 [N][K] (w_q, w_s, w_ts).  bias: bf16 [N] or NULL.
+ * y: bf16 or f32 [M][ldy], ldy >= N.  epi: QA_EPI_GELU_TANH applies
+ * 0.5 v (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))) after the bias.
+ * Accuracy: relative Frobenius error against the exact (float64) product
+ * rounded to the output type is far below 1e-3; the NVFP4 path multiplies
+ * exactly dequantized operands with float32 accumulation; the INT8 path
+ * forms exact int32 sums (see qlinear_int8_acc) and scales them in float.
+ * y must not overlap any input.  Requires 0 < K, K % 16 == 0, M, N >= 0.
+ * ------------------------------------------------------------------------ */
+size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
+int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                  const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                  int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                  void* y, int64_t ldy, qa_out out, qa_epi epi,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+int qlinear_int8(const int8_t* a_q, const float* a_s,
+                 const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                 int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                 void* y, int64_t ldy, qa_out out, qa_epi epi,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The INT8 path's exact integer sums, for verification.  Each NVFP4 weight
+ * row n is written W[n][k] = s_Tw 2^(Fr[n]-11) I[n][k] with an integer I:
+ * an E4M3 scale is M 2^(F-10) (normal: M = 8 + mantissa, F = exponent
+ * field; subnormal: M = mantissa, F = 1), an E2M1 value is c/2 with
+ * c in {0,1,2,3,4,6,8,12}, Fr[n] = the row's smallest F over scales with
+ * M > 0, and I = c M 2^(F - Fr[n]).  Rows whose F spread exceeds 6 are
+ * "irregular"; the others split I = 128 hi + lo, lo in [-64, 63].
+ * acc_hi/acc_lo: int32 [M][N], the exact sums over k of q[m][k] * hi[n][k]
+ * and q[m][k] * lo[n][k]; columns of irregular rows are written as 0.
+ * Uses the qlinear_workspace(QA_INT8, ...) scratch. */
+int qlinear_int8_acc(const int8_t* a_q, const uint8_t* w_q, const uint8_t* w_s,
+                     int64_t M, int64_t N, int64_t K,
+                     int32_t* acc_hi, int32_t* acc_lo,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* act_quant of x followed by the matching qlinear_* (one layer).  For
+ * NVFP4 the tensor scale is computed from x (flags may hold
+ * QA_TSCALE_GIVEN with *x_ts an input); for INT8 x_ts is unused. */
+size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
+int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t flags,
+            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+            int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+            void* y, int64_t ldy, qa_out out, qa_epi epi,
+            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Gamma and the Temporal Delta Cache.  All tensors are bf16 [n] (a whole
+ * block hidden state, flattened); sums are float64 device arrays.  Sums
+ * are deterministic (fixed-order reduction, no atomics) and equal the
+ * exact sums to about 1e-15 relative.
+ *
+ * block_gamma (Fig. 2 and Fig. 3 captions: the block's input/output
+ * relative L1 distance):  sums2 = { sum|out-in|, sum|in| }.
+ *
+ * tdc_update (abstract: the residual between block input and output is
+ * cached; Fig. 4 caption: successive updates compared by relative L2):
+ *   delta_new = bf16(out - in), rounded once, and
+ *   sums4 = { sum|out-in|, sum|in|, sum (delta_new-delta_prev)^2,
+ *             sum delta_prev^2 }  (the last two 0 when delta_prev is NULL).
+ *   delta_new must not overlap in, out or delta_prev.
+ *
+ * tdc_apply (abstract: skip the invariant block):  out = bf16(in + delta),
+ *   rounded once; out may equal in (in place) but must not overlap delta;
+ *   sums2 (nullable) = { sum|out-in|, sum|in| } of the applied pair.
+ * ------------------------------------------------------------------------ */
+size_t reduce_workspace(int64_t n);
+int block_gamma(const uint16_t* in, const uint16_t* out, int64_t n, double* sums2,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+int tdc_update(const uint16_t* in, const uint16_t* out, const uint16_t* delta_prev,
+               uint16_t* delta_new, int64_t n, double* sums4,
+               void* ws, size_t ws_bytes, hipStream_t stream);
+int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
+              double* sums2, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Host-side decisions (pure functions on HOST arrays; no GPU work).
+ *
+ * dmpq_mask (abstract: NVFP4 for temporally stable layers, INT8 for
+ * volatile ones; Fig. 3 caption: E_rel ~ alpha Gamma_{t-1} + beta per
+ * internal linear):  for block l and linear j (entry l*J + j),
+ *   p = alpha[l*J+j] * gamma_prev[l] + beta[l*J+j]   (float64)
+ *   mask = p > tau ? 1 (INT8) : 0 (NVFP4); a tie is NVFP4.
+ *   gamma_prev == NULL (no preceding timestep): every mask entry is 1.
+ *   Gamma values are ratios sum|out-in| / sum|in| (0/0 = 0, x/0 = +inf).
+ *
+ * tdc_decide (Fig. 2 caption: skip from the two preceding block updates):
+ *   skip[l] = t >= 2 && computed_prev[l] && d_prev[l] < delta, where
+ *   d_prev[l] = ||Delta_{t-1} - Delta_{t-2}|| / ||Delta_{t-2}|| from the
+ *   sums of the block's last tdc_update (0/0 = 0, x/0 = +inf).
+ * ------------------------------------------------------------------------ */
+int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha,
+              const float* beta, double tau, uint8_t* mask);
+int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
+               double delta, uint8_t* skip);
+/* Helpers for the host: Gamma and d from the device sums once copied back. */
+double qa_gamma_from_sums(const double* sums2);
+double qa_rel_l2_from_sums(const double* sums4);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QACT_H */

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) quantized-linear library for mixed-precision video DiTs.
+
+The method is 6Bit-Diffusion's inference-time NVFP4/INT8 mixed precision
+(abstract; Fig. 2 and Fig. 3 captions) with the Temporal Delta Cache
+(abstract; Fig. 4 caption).  All work runs in the HIP kernels of
+``libqact.so``; this package only binds its C ABI (``include/qact.h``) and
+allocates buffers with torch.
+"""
+from ._lib import (EPI_GELU_TANH, EPI_NONE, EXPORTS, INT8, LIB_PATH, NVFP4, OUT_BF16, OUT_F32,
+                   TSCALE_GIVEN, QactError, act_quant, act_quant_workspace, block_gamma,
+                   build_info, dmpq_mask, gamma_from_sums, lib, qlinear, qlinear_int8,
+                   qlinear_int8_acc, qlinear_layer_workspace, qlinear_nvfp4, qlinear_workspace,
+                   reduce_workspace, rel_l2_from_sums, strerror, tdc_apply, tdc_decide,
+                   tdc_update)
+from .buffers import (empty_int8_act, empty_nvfp4, workspace)
+
+__all__ = [n for n in dir() if not n.startswith("_")]

@@ -1,0 +1,298 @@
+// C ABI of libqact: argument checks, scratch layout and the host-side
+// decisions of 6Bit-Diffusion (the DMPQ precision rule of the Fig. 3
+// caption and the Temporal Delta Cache skip rule of the Fig. 2 caption).
+// Every device entry point validates everything before it enqueues work.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/qact.h"
+#include "qact_internal.h"
+
+using namespace qact;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // rows / columns / K limit
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return an && bn && x < y + bn && y < x + an;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QA_OK : QA_EHIP; }
+
+int check_mk(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim) return QA_ESHAPE;
+  if (K % 16) return QA_ESHAPE;
+  return QA_OK;
+}
+
+int check_out(qa_out out, qa_epi epi) {
+  if (out != QA_OUT_BF16 && out != QA_OUT_F32) return QA_EINVAL;
+  if (epi != QA_EPI_NONE && epi != QA_EPI_GELU_TANH) return QA_EINVAL;
+  return QA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qa_strerror(int status) {
+  switch (status) {
+    case QA_OK: return "ok";
+    case QA_EINVAL: return "invalid argument (null pointer, bad enum or negative size)";
+    case QA_ESHAPE: return "bad shape (K must be a positive multiple of 16; ld >= K; sizes < 2^31)";
+    case QA_EALIGN: return "misaligned buffer (16-byte alignment required)";
+    case QA_EUNSUPPORTED: return "unsupported combination";
+    case QA_EWORKSPACE: return "workspace too small";
+    case QA_EHIP: return "HIP launch failed";
+    case QA_EALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+const char* qa_build_info(void) { return "libqact 0.1 gfx950"; }
+
+// ------------------------------------------------------------ act_quant --
+
+size_t act_quant_workspace(qa_fmt fmt, int64_t M, int64_t K) {
+  if (fmt == QA_NVFP4) return nvfp4_quant_ws_bytes(M, K);
+  return 0;
+}
+
+int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, void* q,
+              void* scales, float* tscale, uint32_t flags, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  if (fmt != QA_NVFP4 && fmt != QA_INT8) return QA_EINVAL;
+  if (!x || !q || !scales) return QA_EINVAL;
+  if (int s = check_mk(M, K)) return s;
+  if (ldx < K || ldx % 8) return QA_ESHAPE;
+  if (!aligned16(x) || !aligned16(q)) return QA_EALIGN;
+  if (flags & ~QA_TSCALE_GIVEN) return QA_EINVAL;
+  const size_t xbytes = M ? (size_t)((M - 1) * ldx + K) * 2 : 0;
+  if (fmt == QA_INT8) {
+    if (tscale || flags) return QA_EINVAL;
+    if (reinterpret_cast<uintptr_t>(scales) & 3u) return QA_EALIGN;
+    if (overlap(x, xbytes, q, (size_t)(M * K)) || overlap(x, xbytes, scales, (size_t)M * 4))
+      return QA_EALIAS;
+    if (M == 0) return QA_OK;
+    return hip_status(launch_int8_quant(x, M, K, ldx, static_cast<int8_t*>(q),
+                                        static_cast<float*>(scales), stream));
+  }
+  if (!tscale) return QA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(tscale) & 3u) return QA_EALIGN;
+  const bool given = (flags & QA_TSCALE_GIVEN) != 0;
+  if (!given && ws_bytes < nvfp4_quant_ws_bytes(M, K)) return QA_EWORKSPACE;
+  if (!given && !ws) return QA_EINVAL;
+  if (overlap(x, xbytes, q, (size_t)(M * K / 2)) || overlap(x, xbytes, scales, (size_t)(M * K / 16)))
+    return QA_EALIAS;
+  if (M == 0) return QA_OK;
+  return hip_status(launch_nvfp4_quant(x, M, K, ldx, static_cast<uint8_t*>(q),
+                                       static_cast<uint8_t*>(scales), tscale, given, ws, stream));
+}
+
+// -------------------------------------------------------------- qlinear --
+
+size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  return fmt == QA_NVFP4 ? nvfp4_gemm_ws_bytes(M, N, K) : int8_gemm_ws_bytes(M, N, K);
+}
+
+static int check_linear(int64_t M, int64_t N, int64_t K, const void* y, int64_t ldy,
+                        qa_out out, qa_epi epi) {
+  if (int s = check_mk(M, K)) return s;
+  if (N < 0 || N >= kMaxDim) return QA_ESHAPE;
+  if (int s = check_out(out, epi)) return s;
+  if (!y) return QA_EINVAL;
+  if (ldy < N) return QA_ESHAPE;
+  if (reinterpret_cast<uintptr_t>(y) & (out == QA_OUT_F32 ? 3u : 1u)) return QA_EALIGN;
+  return QA_OK;
+}
+
+int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                  const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M,
+                  int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy, qa_out out,
+                  qa_epi epi, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !a_s || !a_ts || !w_q || !w_s || !w_ts) return QA_EINVAL;
+  if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
+  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  if (ws_bytes < nvfp4_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
+  if (!aligned16(ws)) return QA_EALIGN;
+  const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * (out == QA_OUT_F32 ? 4 : 2) : 0;
+  if (overlap(y, ybytes, a_q, (size_t)(M * K / 2)) || overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
+      overlap(y, ybytes, ws, ws_bytes))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
+  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+}
+
+int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
+                 const float* w_ts, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                 void* y, int64_t ldy, qa_out out, qa_epi epi, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  if (!a_q || !a_s || !w_q || !w_s || !w_ts) return QA_EINVAL;
+  if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
+  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  if (ws_bytes < int8_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
+  if (!aligned16(ws)) return QA_EALIGN;
+  const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * (out == QA_OUT_F32 ? 4 : 2) : 0;
+  if (overlap(y, ybytes, a_q, (size_t)(M * K)) || overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
+      overlap(y, ybytes, ws, ws_bytes))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
+  return hip_status(
+      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, nullptr, nullptr, ws, stream));
+}
+
+int qlinear_int8_acc(const int8_t* a_q, const uint8_t* w_q, const uint8_t* w_s, int64_t M,
+                     int64_t N, int64_t K, int32_t* acc_hi, int32_t* acc_lo, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !w_q || !w_s || !acc_hi || !acc_lo) return QA_EINVAL;
+  if (int s = check_mk(M, K)) return s;
+  if (N < 0 || N >= kMaxDim) return QA_ESHAPE;
+  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  if (ws_bytes < int8_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
+  if (M == 0 || N == 0) return QA_OK;
+  // the dump needs no tensor or activation scales (w_ts = null)
+  GemmOut o = {nullptr, 0, 0, 0, nullptr};
+  return hip_status(launch_int8_gemm(a_q, nullptr, w_q, w_s, nullptr, M, N, K, o, acc_hi, acc_lo,
+                                     ws, stream));
+}
+
+size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0) return 0;
+  if (fmt == QA_NVFP4)
+    return round256((size_t)(M * K / 2)) + round256((size_t)(M * K / 16)) +
+           round256(nvfp4_quant_ws_bytes(M, K)) + nvfp4_gemm_ws_bytes(M, N, K);
+  return round256((size_t)(M * K)) + round256((size_t)M * 4) + int8_gemm_ws_bytes(M, N, K);
+}
+
+int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t flags,
+            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
+            int64_t K, const uint16_t* bias, void* y, int64_t ldy, qa_out out, qa_epi epi,
+            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (fmt != QA_NVFP4 && fmt != QA_INT8) return QA_EINVAL;
+  if (!x || !ws) return QA_EINVAL;
+  if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
+  if (ws_bytes < qlinear_layer_workspace(fmt, M, N, K)) return QA_EWORKSPACE;
+  if (!aligned16(ws)) return QA_EALIGN;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  if (fmt == QA_NVFP4) {
+    if (!x_ts) return QA_EINVAL;
+    uint8_t* aq = p;
+    p += round256((size_t)(M * K / 2));
+    uint8_t* as = p;
+    p += round256((size_t)(M * K / 16));
+    void* qws = p;
+    p += round256(nvfp4_quant_ws_bytes(M, K));
+    const size_t gws = nvfp4_gemm_ws_bytes(M, N, K);
+    int s = act_quant(QA_NVFP4, x, M, K, ldx, aq, as, x_ts, flags, qws,
+                      nvfp4_quant_ws_bytes(M, K), stream);
+    if (s) return s;
+    return qlinear_nvfp4(aq, as, x_ts, w_q, w_s, w_ts, M, N, K, bias, y, ldy, out, epi, p, gws,
+                         stream);
+  }
+  if (flags) return QA_EINVAL;
+  int8_t* aq = reinterpret_cast<int8_t*>(p);
+  p += round256((size_t)(M * K));
+  float* as = reinterpret_cast<float*>(p);
+  p += round256((size_t)M * 4);
+  int s = act_quant(QA_INT8, x, M, K, ldx, aq, as, nullptr, 0, nullptr, 0, stream);
+  if (s) return s;
+  return qlinear_int8(aq, as, w_q, w_s, w_ts, M, N, K, bias, y, ldy, out, epi, p,
+                      int8_gemm_ws_bytes(M, N, K), stream);
+}
+
+// ---------------------------------------------------------------- Gamma --
+
+size_t reduce_workspace(int64_t n) { return reduce_ws_bytes(n); }
+
+static int check_stream(const void* a, const void* b, int64_t n, void* ws, size_t ws_bytes,
+                        bool need_ws) {
+  if (!a || !b) return QA_EINVAL;
+  if (n < 0) return QA_EINVAL;
+  if (!aligned16(a) || !aligned16(b)) return QA_EALIGN;
+  if (need_ws && (!ws || ws_bytes < reduce_ws_bytes(n))) return QA_EWORKSPACE;
+  if (need_ws && (reinterpret_cast<uintptr_t>(ws) & 7u)) return QA_EALIGN;
+  return QA_OK;
+}
+
+int block_gamma(const uint16_t* in, const uint16_t* out, int64_t n, double* sums2, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  if (!sums2) return QA_EINVAL;
+  if (int s = check_stream(in, out, n, ws, ws_bytes, true)) return s;
+  return hip_status(launch_tdc(0, in, out, nullptr, nullptr, n, sums2, ws, stream));
+}
+
+int tdc_update(const uint16_t* in, const uint16_t* out, const uint16_t* delta_prev,
+               uint16_t* delta_new, int64_t n, double* sums4, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  if (!sums4 || !delta_new) return QA_EINVAL;
+  if (int s = check_stream(in, out, n, ws, ws_bytes, true)) return s;
+  if (!aligned16(delta_new) || (delta_prev && !aligned16(delta_prev))) return QA_EALIGN;
+  const size_t b = (size_t)n * 2;
+  if (overlap(delta_new, b, in, b) || overlap(delta_new, b, out, b) ||
+      (delta_prev && overlap(delta_new, b, delta_prev, b)) || overlap(delta_new, b, ws, ws_bytes))
+    return QA_EALIAS;
+  return hip_status(launch_tdc(1, in, out, delta_prev, delta_new, n, sums4, ws, stream));
+}
+
+int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
+              double* sums2, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!out) return QA_EINVAL;
+  if (int s = check_stream(in, delta, n, ws, ws_bytes, sums2 != nullptr)) return s;
+  if (!aligned16(out)) return QA_EALIGN;
+  const size_t b = (size_t)n * 2;
+  if (overlap(out, b, delta, b)) return QA_EALIAS;
+  if (out != in && overlap(out, b, in, b)) return QA_EALIAS;
+  return hip_status(launch_tdc(2, in, delta, nullptr, out, n, sums2, ws, stream));
+}
+
+// ------------------------------------------------------ host decisions --
+
+static double ratio0(double num, double den) {
+  if (den == 0.0) return num == 0.0 ? 0.0 : INFINITY;
+  return num / den;
+}
+
+double qa_gamma_from_sums(const double* sums2) {
+  return sums2 ? ratio0(sums2[0], sums2[1]) : NAN;
+}
+
+double qa_rel_l2_from_sums(const double* sums4) {
+  return sums4 ? ratio0(sqrt(sums4[2]), sqrt(sums4[3])) : NAN;
+}
+
+int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha, const float* beta,
+              double tau, uint8_t* mask) {
+  if (L < 0 || J <= 0 || !mask) return QA_EINVAL;
+  if (gamma_prev && (!alpha || !beta)) return QA_EINVAL;
+  for (int l = 0; l < L; ++l)
+    for (int j = 0; j < J; ++j) {
+      const int i = l * J + j;
+      if (!gamma_prev) {
+        mask[i] = 1;
+        continue;
+      }
+      const double p = (double)alpha[i] * gamma_prev[l] + (double)beta[i];
+      mask[i] = p > tau ? 1 : 0;
+    }
+  return QA_OK;
+}
+
+int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L, double delta,
+               uint8_t* skip) {
+  if (L < 0 || !skip || (L && t >= 2 && (!d_prev || !computed_prev))) return QA_EINVAL;
+  for (int l = 0; l < L; ++l)
+    skip[l] = (t >= 2 && computed_prev[l] && d_prev[l] < delta) ? 1 : 0;
+  return QA_OK;
+}
+
+}  // extern "C"

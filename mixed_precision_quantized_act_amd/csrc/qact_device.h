@@ -1,0 +1,78 @@
+// Device helpers shared by the gfx950 kernels of libqact: bfloat16 bit
+// handling and the E2M1 / E4M3 encoders and decoders of the NVFP4 format
+// (E2M1 elements, one E4M3 scale per 16, one float32 tensor scale), rounding
+// to nearest with ties to the even code and saturating.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qact {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs; overflow
+// rounds to infinity as round-to-nearest prescribes).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 1/y, and 0 for y == 0 (correctly rounded float32 division).
+__device__ __forceinline__ float recip0(float y) { return y == 0.0f ? 0.0f : 1.0f / y; }
+
+// E4M3FN code (0..0x7E) of a finite float32 scale s >= 0: nearest value,
+// ties to the even code, saturating at 448 (0x7E).
+//   normal range (s >= 2^-6): round the float32 encoding to 3 mantissa
+//   bits (a carry moves into the exponent), then rebias 127 -> 7;
+//   below 2^-6 the E4M3 step is 2^-9: code = rint(s * 512), up to 8 = 0x08.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (s < 0.015625f) return (uint32_t)rintf(s * 512.0f);
+  uint32_t u = __float_as_uint(s);
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;   // exp8:mant3
+  r -= (127u - 7u) << 3;
+  return r > 0x7Eu ? 0x7Eu : r;
+}
+
+// Value of a non-negative E4M3FN code 0..0x7E.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;               // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 code of a float32 value: nearest of 0,.5,1,1.5,2,3,4,6 with ties to
+// the even code, saturating; bit 3 = the sign bit of v.  Each decision
+// threshold sits on a tie, which belongs to the even code: 0|1 at .25 (>),
+// 1|2 at .75 (>=), 2|3 at 1.25 (>), 3|4 at 1.75 (>=), 4|5 at 2.5 (>),
+// 5|6 at 3.5 (>=), 6|7 at 5 (>).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// E2M1 value times 2 (an integer in -12..12) of a 4-bit code.
+__device__ __forceinline__ int e2m1_twice(uint32_t c) {
+  const int mag = (int)((0xC8643210u >> ((c & 7u) * 4u)) & 0xFu);   // 0,1,2,3,4,6,8,12
+  return (c & 8u) ? -mag : mag;
+}
+
+// Wave-level (64 lanes) reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace qact

@@ -1,0 +1,43 @@
+// Internal launch entry points of libqact (host side).  Each returns the
+// HIP error of its launches; argument checking is done by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qact {
+
+// ---- activation quantization (act_quant.hip)
+size_t nvfp4_quant_ws_bytes(int64_t M, int64_t K);
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              uint8_t* q, uint8_t* scales, float* tscale, bool given,
+                              void* ws, hipStream_t stream);
+hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                             float* scale, hipStream_t stream);
+
+// ---- quantized GEMMs (qgemm.hip)
+struct GemmOut {
+  void* y;
+  int64_t ldy;
+  int out_f32;            // 0: bf16, 1: f32
+  int gelu;               // 0: none, 1: GELU-tanh
+  const uint16_t* bias;   // bf16 [N] or null
+};
+size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                             const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                             int64_t M, int64_t N, int64_t K, const GemmOut& o, void* ws,
+                             hipStream_t stream);
+size_t int8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                            const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
+                            int64_t K, const GemmOut& o, int32_t* acc_hi, int32_t* acc_lo,
+                            void* ws, hipStream_t stream);
+
+// ---- Gamma / Temporal Delta Cache (tdc.hip)
+size_t reduce_ws_bytes(int64_t n);
+// mode 0: block_gamma, 1: tdc_update, 2: tdc_apply
+hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* delta_prev,
+                      uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream);
+
+}  // namespace qact

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, rejects bad arguments before any launch, and its host-side
+decisions equal the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mixed_precision_quantized_act_amd as qa
+from oracle import tdc as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qact.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\(", src, flags=re.M))
+
+
+def test_every_declared_symbol_exported_and_bound():
+    declared = _declared()
+    assert {"act_quant", "qlinear_nvfp4", "qlinear_int8", "block_gamma", "tdc_update",
+            "tdc_apply", "dmpq_mask", "tdc_decide"} <= declared
+    lib = qa.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(qa.EXPORTS)
+
+
+def test_build_info():
+    assert "gfx950" in qa.build_info()
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10008)
+
+
+def _status(fn, *args):
+    return getattr(qa.lib(), fn)(*args)
+
+
+def test_act_quant_validation():
+    assert _status("act_quant", 0, None, 4, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -1
+    assert _status("act_quant", 0, FAKE, 4, 24, 24, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -2
+    assert _status("act_quant", 0, FAKE, 4, 16, 8, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -2
+    assert _status("act_quant", 0, FAKE_ODD, 4, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -3
+    assert _status("act_quant", 0, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 0, None) == -5
+    assert _status("act_quant", 7, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -1
+    assert _status("act_quant", 1, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, None, 0, None) == -1
+    assert _status("act_quant", 0, FAKE, -1, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -2
+    assert _status("act_quant", 0, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 2, FAKE, 1 << 20, None) == -1
+    # q overlapping x
+    assert _status("act_quant", 1, FAKE, 4, 16, 16, FAKE, ctypes.c_void_p(0x20000), None, 0,
+                   None, 0, None) == -7
+
+
+def test_qlinear_validation():
+    big = 1 << 40
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 24, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, big, None) == -2
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 3, 0, 0, FAKE, big, None) == -2
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 5, 0, FAKE, big, None) == -1
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 9, FAKE, big, None) == -1
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
+    assert _status("qlinear_nvfp4", None, *ok[1:], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, big, None) == -1
+    assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900001), 4, 0, 0, FAKE, big, None) == -3
+    assert qa.qlinear_workspace(qa.NVFP4, 17776, 5760, 1920) > 17776 * 1920 * 2
+    assert qa.qlinear_workspace(qa.INT8, 17776, 5760, 1920) >= 2 * 5760 * 1920
+
+
+def test_tdc_validation():
+    assert _status("tdc_update", FAKE, FAKE, None, FAKE, 64, FAKE, FAKE, 1 << 20, None) == -7
+    assert _status("tdc_update", FAKE, FAKE, None, FAKE_ODD, 64, FAKE, FAKE, 1 << 20, None) == -3
+    assert _status("tdc_update", FAKE, FAKE, None, ctypes.c_void_p(0x900000), 64, FAKE, FAKE, 0, None) == -5
+    assert _status("tdc_apply", FAKE, ctypes.c_void_p(0x10040), ctypes.c_void_p(0x10040), 64, None, None, 0, None) == -7
+    assert _status("tdc_apply", FAKE, ctypes.c_void_p(0x900000), ctypes.c_void_p(0x10020), 64, None, None, 0, None) == -7
+    assert _status("block_gamma", FAKE, FAKE, -1, FAKE, FAKE, 1 << 20, None) == -1
+    assert _status("block_gamma", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
+
+
+def test_strerror_covers_codes():
+    for s in range(-7, 1):
+        assert qa.strerror(s) != "unknown status"
+
+
+def test_dmpq_mask_matches_oracle():
+    rng = np.random.default_rng(0)
+    L, J = 42, 4
+    g = rng.uniform(0, 0.2, L)
+    alpha = rng.uniform(0.5, 1.5, L * J).astype(np.float32)
+    beta = rng.uniform(0, 0.02, L * J).astype(np.float32)
+    for tau in (0.05, 0.1, 0.15):
+        np.testing.assert_array_equal(qa.dmpq_mask(g, alpha, beta, tau, L, J),
+                                      T.dmpq_mask(g, alpha, beta, tau, J))
+    np.testing.assert_array_equal(qa.dmpq_mask(None, alpha, beta, 0.1, L, J),
+                                  T.dmpq_mask(None, alpha, beta, 0.1, J))
+    # the worked tie: p == tau -> NVFP4
+    p = float(np.float32(1.0)) * 0.125 + float(np.float32(2.0 ** -7))
+    assert qa.dmpq_mask([0.125], [1.0], [2.0 ** -7], p, 1, 1)[0] == 0
+    assert qa.dmpq_mask([0.125], [1.0], [2.0 ** -7], 0.125, 1, 1)[0] == 1
+
+
+def test_tdc_decide_matches_oracle():
+    rng = np.random.default_rng(1)
+    d = rng.uniform(0, 0.1, 30)
+    d[3] = 0.05
+    c = rng.integers(0, 2, 30).astype(np.uint8)
+    for t in range(4):
+        np.testing.assert_array_equal(qa.tdc_decide(t, d, c, 0.05), T.tdc_decide(t, d, c, 0.05))
+
+
+def test_sum_helpers():
+    assert qa.gamma_from_sums([0.0, 0.0]) == 0.0
+    assert qa.gamma_from_sums([1.0, 0.0]) == float("inf")
+    assert qa.rel_l2_from_sums([0, 0, 6.25 * 2.0 ** -10, 6.25]) == 0.03125
