@@ -1,0 +1,264 @@
+"""Benchmark of the quantized-linear hot path on one MI355X.
+
+Workload: the CogVideoX-2B-shaped QKV projection, M = 17776 tokens (17550
+video + 226 text), K = 1920, N = 5760, bf16 activations ~N(0,1) with 1 %
+outlier channels x30, weights ~N(0, 0.02^2) quantized to NVFP4 once at set
+up.  The pages measure on VBench with trained CogVideoX weights; seeded
+synthetic tensors of the same shapes stand in for them.
+
+One step is one pass of the whole hot path over that batch:
+  act_quant NVFP4 -> qlinear_nvfp4 ; act_quant INT8 -> qlinear_int8 ;
+  tdc_update (Delta cache, with Gamma and relative-L2 sums) ;
+  tdc_apply (the skip path, with Gamma sums) ;
+  copy of the sums to the host, dmpq_mask and tdc_decide.
+`value` is the linear FLOPs of both activation paths per second of whole
+steps (2 * 2*M*N*K per step).  Per-kernel times come from HIP events on
+the launch stream inside the timed steps; the GEMM kernels are bracketed
+by the library's event hook, so their time excludes operand preparation.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "int8_TOPs": 5000.0, "fp4_TFLOPs": 10100.0,
+        "fp8_TFLOPs": 5000.0}
+M, K, N = 17776, 1920, 5760
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def cpu_baseline(x, w, x_out, delta_prev, rows):
+    """The oracle, untuned, on the first `rows` token rows of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as G
+    from oracle import quant as Q
+    from oracle import tdc as T
+    wq = Q.nvfp4_encode(w)                     # set-up, untimed as on the GPU
+    wd = Q.nvfp4_decode(*wq)
+    xs, xo, dp = x[:rows], x_out[:rows], delta_prev[:rows]
+    t0 = time.perf_counter()
+    a4 = Q.nvfp4_encode(xs)
+    G.linear_ref(Q.nvfp4_decode(*a4), wd)
+    a8 = Q.int8_encode(xs)
+    G.linear_ref(Q.int8_decode(*a8), wd)
+    dn, sums = T.tdc_update(xs.ravel(), xo.ravel(), dp.ravel())
+    applied = T.tdc_apply(xs.ravel(), dn)
+    T.gamma_sums(xs.ravel(), applied)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    flops = 2 * 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {rows} of {M} token rows, one full step (both quantizers, both "
+                      f"float64 GEMMs, TDC update/apply sums), {dt:.1f} s; element-wise numpy on "
+                      f"1 thread, float64 BLAS on {cores} threads; host has {os.cpu_count()} CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the quantized-linear path has no multi-GPU "
+              "variant in this library (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixed_precision_quantized_act_amd as qa
+    import synth
+
+    qa.lib()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a.copy()).to(dev)
+
+    x, w = synth.linear_case(2)
+    x_out = synth.gamma_pair(2, x)                 # the block output paired with x
+    delta_prev = synth.bf16_bits(np.random.default_rng([2, 60]).standard_normal(x.shape) * 0.1)
+    xd, wd, xod, dpd = to_dev(x), to_dev(w), to_dev(x_out), to_dev(delta_prev)
+    n = M * K
+
+    wq, wsc, wts = qa.empty_nvfp4(N, K, dev)
+    qa.act_quant(qa.NVFP4, wd, wq, wsc, wts, 0, qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K), dev))
+    aq, asc, ats = qa.empty_nvfp4(M, K, dev)
+    qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K), dev)
+    a8, s8 = qa.empty_int8_act(M, K, dev)
+    y4 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y8 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws4 = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, N, K), dev)
+    ws8 = qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K), dev)
+    dnew = torch.empty(n, dtype=torch.int16, device=dev)
+    applied = torch.empty(n, dtype=torch.int16, device=dev)
+    s4 = torch.zeros(4, dtype=torch.float64, device=dev)
+    s2 = torch.zeros(2, dtype=torch.float64, device=dev)
+    rws = qa.workspace(qa.reduce_workspace(n), dev)
+    host_sums = torch.zeros(6, dtype=torch.float64).pin_memory()
+    alpha = np.ones(4, np.float32)
+    beta = np.full(4, 0.01, np.float32)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    names = ["act_quant_nvfp4", "qlinear_nvfp4", "gemm_nvfp4", "act_quant_int8", "qlinear_int8",
+             "gemm_int8", "tdc_update", "tdc_apply"]
+    ev = {k: [] for k in names}
+
+    def step(timed, t):
+        pairs = {}
+
+        def bracket(name, fn):
+            if not timed:
+                fn()
+                return
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            pairs[name] = (a, b)
+
+        def gemm(name, fn):
+            if timed:
+                a, b = hip.event(), hip.event()
+                qa.set_gemm_events(a.value, b.value)
+                pairs[name] = (a, b)
+            fn()
+            if timed:
+                qa.set_gemm_events(None, None)
+
+        bracket("act_quant_nvfp4", lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws))
+        bracket("qlinear_nvfp4", lambda: gemm("gemm_nvfp4", lambda: qa.qlinear_nvfp4(
+            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4)))
+        bracket("act_quant_int8", lambda: qa.act_quant(qa.INT8, xd, a8, s8))
+        bracket("qlinear_int8", lambda: gemm("gemm_int8", lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8)))
+        bracket("tdc_update", lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws))
+        bracket("tdc_apply", lambda: qa.tdc_apply(xd, dnew, applied, s2, rws))
+        host_sums[:4].copy_(s4, non_blocking=True)
+        host_sums[4:].copy_(s2, non_blocking=True)
+        torch.cuda.current_stream(dev).synchronize()
+        h = host_sums.numpy()
+        g = qa.gamma_from_sums(h[4:6])
+        d = qa.rel_l2_from_sums(h[:4])
+        qa.dmpq_mask(np.array([g]), alpha, beta, 0.1, 1, 4)
+        qa.tdc_decide(t, [d], [1], 0.05)
+        return pairs
+
+    for t in range(args.warmup):
+        step(False, t)
+    torch.cuda.synchronize()
+    all_pairs = []
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        all_pairs.append(step(True, t))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for pairs in all_pairs:
+        for k, (a, b) in pairs.items():
+            ev[k].append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+    avg = {k: float(np.mean(v)) for k, v in ev.items() if v}
+
+    ms_step = wall * 1e3 / args.steps
+    flops_step = 2 * 2.0 * M * N * K
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    def tf(ms):
+        return 2.0 * M * N * K / (ms * 1e-3) / 1e12
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    kern = {
+        "gemm_nvfp4": {"us": avg["gemm_nvfp4"] * 1e3, "TFLOP/s": tf(avg["gemm_nvfp4"]),
+                       "issued_dtype": "bf16 MFMA on exactly dequantized NVFP4",
+                       "frac_bf16_peak": tf(avg["gemm_nvfp4"]) / PEAK["bf16_TFLOPs"],
+                       "frac_fp4_peak": tf(avg["gemm_nvfp4"]) / PEAK["fp4_TFLOPs"]},
+        "qlinear_nvfp4_call": {"us": avg["qlinear_nvfp4"] * 1e3, "TFLOP/s": tf(avg["qlinear_nvfp4"])},
+        "gemm_int8": {"us": avg["gemm_int8"] * 1e3, "TOP/s": tf(avg["gemm_int8"]),
+                      "issued_dtype": "int8 MFMA, two weight digit planes",
+                      "frac_int8_peak": tf(avg["gemm_int8"]) / PEAK["int8_TOPs"]},
+        "qlinear_int8_call": {"us": avg["qlinear_int8"] * 1e3, "TOP/s": tf(avg["qlinear_int8"])},
+        "act_quant_nvfp4": {"us": avg["act_quant_nvfp4"] * 1e3,
+                            "GB/s": gbs(2.5625 * n, avg["act_quant_nvfp4"])},
+        "act_quant_int8": {"us": avg["act_quant_int8"] * 1e3,
+                           "GB/s": gbs(3.0 * n + 4 * M, avg["act_quant_int8"])},
+        "tdc_update": {"us": avg["tdc_update"] * 1e3, "GB/s": gbs(8.0 * n, avg["tdc_update"])},
+        "tdc_apply": {"us": avg["tdc_apply"] * 1e3, "GB/s": gbs(6.0 * n, avg["tdc_apply"])},
+    }
+    for k in ("act_quant_nvfp4", "act_quant_int8", "tdc_update", "tdc_apply"):
+        kern[k]["frac_hbm"] = kern[k]["GB/s"] / PEAK["hbm_GBps"]
+    for v in kern.values():
+        for kk in list(v):
+            if isinstance(v[kk], float):
+                v[kk] = round(v[kk], 4)
+
+    # dominant kernel: the longest of the two GEMM kernels
+    if avg["gemm_int8"] >= avg["gemm_nvfp4"]:
+        dom, ach, peak, dt = "gemm_int8", tf(avg["gemm_int8"]), PEAK["int8_TOPs"], "int8"
+    else:
+        dom, ach, peak, dt = "gemm_nvfp4", tf(avg["gemm_nvfp4"]), PEAK["bf16_TFLOPs"], "bf16"
+    roofline = {"bound": "mfma", "kernel": dom, "dtype": dt, "achieved": round(ach, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+
+    line = {
+        "metric": "qlinear TFLOP/s (NVFP4 & INT8 A-paths) + quant/TDC GB/s, % of roofline",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4+int8 (bf16/i8 MFMA)",
+        "data": "synthetic",
+        "config": {"workload": "cogvideox2b-qkv", "M": M, "K": K, "N": N,
+                   "activations": "N(0,1) bf16, 19 outlier channels x30",
+                   "weights": "N(0,0.02^2) -> NVFP4", "parallelism": "none (1 GPU)"},
+        "kernels": kern,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, w, x_out, delta_prev, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -193,6 +193,13 @@ int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha,
               const float* beta, double tau, uint8_t* mask);
 int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
                double delta, uint8_t* skip);
+/* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
+ * inside qlinear) records `before` on its stream just before its main GEMM
+ * kernel and `after` just after it, so that the caller can time that kernel
+ * alone with hipEventElapsedTime.  The events are created and owned by the
+ * caller; pass NULL, NULL to stop.  Process-wide setting, not thread-safe. */
+int qa_set_gemm_events(hipEvent_t before, hipEvent_t after);
+
 /* Helpers for the host: Gamma and d from the device sums once copied back. */
 double qa_gamma_from_sums(const double* sums2);
 double qa_rel_l2_from_sums(const double* sums4);

@@ -49,6 +49,7 @@ _SIGS = {
     "tdc_apply": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "dmpq_mask": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_double, _P]),
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
+    "qa_set_gemm_events": (ctypes.c_int, [_P, _P]),
     "qa_gamma_from_sums": (ctypes.c_double, [_P]),
     "qa_rel_l2_from_sums": (ctypes.c_double, [_P]),
 }
@@ -205,6 +206,12 @@ def tdc_decide(t, d_prev, computed_prev, delta):
     _check("tdc_decide", lib().tdc_decide(int(t), d.ctypes.data_as(_P), c.ctypes.data_as(_P),
                                           len(d), float(delta), skip.ctypes.data_as(_P)))
     return skip
+
+
+def set_gemm_events(before, after):
+    """Record raw hipEvent_t handles (ints) around every main GEMM kernel;
+    (None, None) stops."""
+    _check("qa_set_gemm_events", lib().qa_set_gemm_events(before, after))
 
 
 def gamma_from_sums(sums2):

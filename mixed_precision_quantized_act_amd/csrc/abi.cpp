@@ -255,6 +255,12 @@ int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t 
   return hip_status(launch_tdc(2, in, delta, nullptr, out, n, sums2, ws, stream));
 }
 
+int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
+  set_gemm_events(before, after);
+  return QA_OK;
+}
+
 // ------------------------------------------------------ host decisions --
 
 static double ratio0(double num, double den) {

@@ -389,14 +389,27 @@ size_t int8_gemm_ws_bytes(int64_t, int64_t N, int64_t K) {
   return (size_t)round_up(2 * np * kp, 256) + (size_t)round_up(np * 4, 256) + (size_t)np;
 }
 
+static hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+void set_gemm_events(hipEvent_t before, hipEvent_t after) {
+  g_ev_before = before;
+  g_ev_after = after;
+}
+
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
   const int total = g.mt * g.nt;
   const int grid = 8 * ((total + 7) / 8);
+  if (g_ev_before) {
+    hipError_t err = hipEventRecord(g_ev_before, st);
+    if (err != hipSuccess) return err;
+  }
   if (i8)
     hipLaunchKernelGGL(qgemm_kernel<true>, dim3(grid), dim3(kThreads), 0, st, g, e);
   else
     hipLaunchKernelGGL(qgemm_kernel<false>, dim3(grid), dim3(kThreads), 0, st, g, e);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && g_ev_after) err = hipEventRecord(g_ev_after, st);
+  return err;
 }
 
 hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
