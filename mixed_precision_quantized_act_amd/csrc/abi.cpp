@@ -6,7 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/qact.h"
+#include "qact.h"
 #include "qact_internal.h"
 
 using namespace qact;

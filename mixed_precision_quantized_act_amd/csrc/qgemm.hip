@@ -35,15 +35,17 @@ namespace qact {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(16))) int i32x16;
 
-static constexpr int kThreads = 256;
 static constexpr int kTileM = 256;
 static constexpr int kTileRowsB = 256;        // B tile rows per stage (bf16: N; int8: 2 x 128)
 static constexpr int kRowBytes = 128;         // bytes per tile row per K stage
 static constexpr int kStageBytes = (kTileM + kTileRowsB) * kRowBytes;
 static constexpr int kGroupM = 8;
+static constexpr int kEpiStride = 72;         // floats per staged output row
+static constexpr int kSmemBytes = 4 * 128 * kEpiStride * 4;   // >= 2 operand stages
 
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -154,6 +156,7 @@ struct EpiArgs {
   int gelu;
   const uint16_t* bias;
   int64_t M, N;
+  int vec_ok;            // y 16-byte aligned and ldy % 4 == 0: vector stores
 };
 
 __device__ __forceinline__ void store_out(const EpiArgs& e, int64_t row, int64_t col, float v) {
@@ -186,16 +189,58 @@ struct GemmArgs {
   int32_t* acc_lo;
 };
 
-template <bool I8>
-__device__ __forceinline__ int b_tile_row(int wn, int j, int lane) {
-  if (I8) return (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31);
-  return wn * 128 + j * 32 + (lane & 31);
+// Wave grid of a workgroup: WM x WN waves (WM = 2).  A wave owns a
+// (256/WM) x (256/WN) block of the 256 x 256 output tile (INT8: (256/WM) x
+// (128/WN) columns of each of the two digit planes), as FM x FN MFMA tiles
+// of 32 x 32.
+template <int WN>
+struct Cfg {
+  static constexpr int WM = 2;
+  static constexpr int NW = WM * WN;              // waves
+  static constexpr int NT = 64 * NW;              // threads
+  static constexpr int FM = 256 / WM / 32;        // A fragments per wave
+  static constexpr int FN = 256 / WN / 32;        // B fragments per wave
+  static constexpr int RPP = NT / 8;              // tile rows per staging pass
+  static constexpr int PASSES = 256 / RPP;        // staging passes per operand
+  static constexpr int EP_FM = NW == 4 ? 4 : 2;   // A fragments per epilogue pass
+};
+
+template <bool I8, int WN>
+__device__ __forceinline__ int b_frag_row(int wn, int j, int lane) {
+  constexpr int FN = Cfg<WN>::FN;
+  if (I8) {
+    constexpr int half = FN / 2;                  // column fragments per digit plane
+    return (j / half) * 128 + wn * (128 / WN) + (j % half) * 32 + (lane & 31);
+  }
+  return wn * (256 / WN) + j * 32 + (lane & 31);
 }
 
-template <bool I8>
-__global__ void __launch_bounds__(kThreads, 1)
+// LDS swizzle: 16-byte chunk c of tile row r sits in chunk slot
+// c ^ ((r >> 1) & 7) of its 128-byte row.  A 16-lane group of a 16-byte
+// fragment read covers 16 consecutive rows at one chunk: even rows land in
+// one half of the 64 banks and odd rows in the other, and (r >> 1) & 7
+// spreads each half's 8 rows over the 8 slots, so the group hits 64
+// distinct banks.  The staging writes (8 lanes per row) are conflict-free
+// too.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer (stride 0): loads at offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <bool I8, bool DUMP, int WN>
+__global__ void __launch_bounds__(Cfg<WN>::NT, 1)
 qgemm_kernel(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  using C = Cfg<WN>;
+  static_assert(kSmemBytes >= 2 * kStageBytes, "LDS holds two operand stages");
+  static_assert(C::NW * C::EP_FM * 32 * kEpiStride * 4 <= kSmemBytes, "epilogue staging fits");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
 
   // XCD-aware tile order: hardware deals workgroups to the 8 XCDs in turn;
   // give each XCD a contiguous range of logical tiles, grouped kGroupM
@@ -214,168 +259,250 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   const int64_t nb0 = (int64_t)tn * (I8 ? 128 : 256);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
-  // global -> register staging: per K stage each thread moves 8 chunks of
-  // 16 bytes of A and 8 of B; chunk i covers tile row i*32 + tid/8, byte
-  // column (tid%8)*16, so rows step by 32 and the LDS slot by 32 rows.
+  // Buffer resources based at this tile's first row: rows past the operand
+  // (INT8 activations: rows >= M) fall outside the range and load zero.
+  int64_t a_bytes = (g.a_rows - m0) * g.lda;
+  if (a_bytes > 0x7FFFFFF0) a_bytes = 0x7FFFFFF0;
+  const __amdgpu_buffer_rsrc_t ra_src = buffer_rsrc(g.A + m0 * g.lda, (uint32_t)a_bytes);
+  const __amdgpu_buffer_rsrc_t rb_src = buffer_rsrc(g.B + nb0 * g.ldb, 0x7FFFFFF0u);
+
+  // global -> register staging: per K stage each thread moves PASSES chunks
+  // of 16 bytes of A and of B; chunk i covers tile row i*RPP + tid/8, byte
+  // column (tid%8)*16 (RPP is a multiple of 16, so every chunk of a thread
+  // has the same swizzle).
   const int r8 = tid >> 3, ch8 = tid & 7;
-  const int lds_base = r8 * kRowBytes + ((ch8 ^ (r8 & 7)) << 4);
-  const uint8_t* b_base = g.B + (nb0 + r8) * g.ldb + ch8 * 16;
-  u32x4 ra[8], rb[8];
-  auto load_stage = [&](int kt) {
-    const int64_t kb = (int64_t)kt * kRowBytes;
-    // only the INT8 activation operand is the caller's unpadded buffer:
-    // its rows past M are clamped (the results are not stored) and its
-    // K chunks past K load as zero
-    const bool kin = !I8 || kb + ch8 * 16 < g.a_kbytes;
+  const int lds_base = r8 * kRowBytes + ((ch8 ^ swz(r8)) << 4);
+  const uint32_t a_off = (uint32_t)(r8 * g.lda + ch8 * 16);
+  const uint32_t a_step = (uint32_t)(C::RPP * g.lda);
+  const uint32_t b_off = (uint32_t)(r8 * g.ldb + ch8 * 16);
+  u32x4 ra[C::PASSES], rb[C::PASSES];
+  auto gload = [&](int kt) {
+    const uint32_t kb = (uint32_t)kt * kRowBytes;
+    // the INT8 activation rows are unpadded: a chunk past K loads zero
+    const bool kin = !I8 || (int64_t)kb + ch8 * 16 < g.a_kbytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t ar = m0 + i * 32 + r8;
-      if (I8) ar = ar < g.a_rows ? ar : g.a_rows - 1;
-      if (kin)
-        ra[i] = *reinterpret_cast<const u32x4*>(g.A + ar * g.lda + kb + ch8 * 16);
-      else
-        ra[i] = u32x4{0, 0, 0, 0};
-      const int64_t boff = I8 ? (int64_t)(i >> 2) * g.b_plane + (int64_t)((i & 3) * 32) * g.ldb
-                              : (int64_t)(i * 32) * g.ldb;
-      rb[i] = *reinterpret_cast<const u32x4*>(b_base + boff + kb);
+    for (int i = 0; i < C::PASSES; ++i) {
+      ra[i] = buffer_load16(ra_src, kin ? a_off + i * a_step + kb : 0x7FFFFFF0u);
+      const int trow = i * C::RPP;                // first tile row of this pass
+      const uint32_t bo = I8 ? (uint32_t)(trow / 128) * (uint32_t)g.b_plane +
+                                   (uint32_t)((trow % 128) * g.ldb)
+                             : (uint32_t)(trow * g.ldb);
+      rb[i] = buffer_load16(rb_src, b_off + bo + kb);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto lds_store = [&](int buf) {
     uint8_t* sa = smem + buf * kStageBytes + lds_base;
     uint8_t* sb = sa + kTileM * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(sa + i * 32 * kRowBytes) = ra[i];
-      *reinterpret_cast<u32x4*>(sb + i * 32 * kRowBytes) = rb[i];
+    for (int i = 0; i < C::PASSES; ++i) {
+      *reinterpret_cast<u32x4*>(sa + i * C::RPP * kRowBytes) = ra[i];
+      *reinterpret_cast<u32x4*>(sb + i * C::RPP * kRowBytes) = rb[i];
     }
   };
 
   typedef typename std::conditional<I8, i32x16, f32x16>::type acc_t;
-  acc_t acc[4][4];
+  acc_t acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  int a_frag_off[4], b_frag_off[4];
+  // fragment rows of this lane are (multiple of 32) + lane % 32, so they
+  // all share the swizzle of lane % 32
+  const int a_frag = (wm * (256 / C::WM) + (lane & 31)) * kRowBytes;
+  const int row_sw = swz(lane & 31);
+  auto frags = [&](int buf, int s, u32x4 (&af)[C::FM], u32x4 (&bf)[C::FN]) {
+    const uint8_t* sa = smem + buf * kStageBytes;
+    const uint8_t* sb = sa + kTileM * kRowBytes;
+    const int coff = ((2 * s + (lane >> 5)) ^ row_sw) << 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_frag_off[i] = (wm * 128 + i * 32 + (lane & 31)) * kRowBytes;
-    b_frag_off[i] = b_tile_row<I8>(wn, i, lane) * kRowBytes;
-  }
-  const int row_sw = lane & 7;           // (row & 7) of every fragment row of this lane
+    for (int i = 0; i < C::FM; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(sa + a_frag + i * 32 * kRowBytes + coff);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(sb + b_frag_row<I8, WN>(wn, j, lane) * kRowBytes +
+                                              coff);
+  };
+  auto mfmas = [&](const u32x4 (&af)[C::FM], const u32x4 (&bf)[C::FN]) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (I8)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, af[i]),
+                                                            __builtin_bit_cast(i32x4, bf[j]),
+                                                            acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, bf[j]),
+                                                              acc[i][j], 0, 0, 0);
+      }
+  };
 
-  load_stage(0);
-  store_stage(0);
+  // Pipeline: LDS holds stage kt while registers carry stage kt+1 from
+  // global memory; fragments of substep s+1 are read while the MFMAs of
+  // substep s run.  At substep 3 the next stage goes to the other LDS
+  // buffer (one barrier per stage) and the loads of stage kt+2 are issued.
+  gload(0);
+  lds_store(0);
   __syncthreads();
+  if (g.k_tiles > 1) gload(1);
+  u32x4 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < g.k_tiles; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < g.k_tiles;
-    if (more) load_stage(kt + 1);
-    const uint8_t* sa = smem + cur * kStageBytes;
-    const uint8_t* sb = sa + kTileM * kRowBytes;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = 2 * s + (lane >> 5);
-      const int coff = (ch ^ row_sw) << 4;
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const u32x4*>(sa + a_frag_off[i] + coff);
-        bf[i] = *reinterpret_cast<const u32x4*>(sb + b_frag_off[i] + coff);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (I8)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                __builtin_bit_cast(i32x4, af[i]), __builtin_bit_cast(i32x4, bf[j]), acc[i][j], 0,
-                0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[j]), acc[i][j],
-                0, 0, 0);
-        }
+    frags(cur, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    frags(cur, 2, fa0, fb0);
+    mfmas(fa1, fb1);
+    frags(cur, 3, fa1, fb1);
+    mfmas(fa0, fb0);
+    if (kt + 1 < g.k_tiles) {
+      lds_store(cur ^ 1);
+      __syncthreads();
+      frags(cur ^ 1, 0, fa0, fb0);
+      if (kt + 2 < g.k_tiles) gload(kt + 2);
     }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
+    mfmas(fa1, fb1);
   }
 
-  // epilogue: accumulator r of a 32x32 tile holds row (r/4)*8 + (lane/32)*4
-  // + r%4 and column lane%32
-  const int64_t row_base = m0 + wm * 128 + (lane >> 5) * 4;
-  if constexpr (I8) {
+  // ---- epilogue.  Accumulator r of a 32x32 MFMA tile holds row
+  // (r/4)*8 + (lane/32)*4 + r%4 and column lane%32.  In passes of EP_FM row
+  // fragments x 64 columns, each wave stages its values as float32 in LDS
+  // (row stride kEpiStride floats: the two half-waves write disjoint
+  // banks), then reads them back row-contiguous and stores 4 consecutive
+  // outputs per lane.
+  __syncthreads();                       // every wave is done with the operand tiles
+  const int lrow = (lane >> 5) * 4, lcol = lane & 31;
+  constexpr int OUT_FRAGS = I8 ? C::FN / 2 : C::FN;     // 32-column output blocks per wave
+  const int64_t wave_row0 = m0 + wm * (256 / C::WM);
+  const int64_t wave_col0 = nb0 + wn * (OUT_FRAGS * 32);
+  if constexpr (I8 && DUMP) {          // verification dump of the exact sums
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const int64_t col = nb0 + wn * 64 + jn * 32 + (lane & 31);
-      const bool col_ok = col < e.N;
-      const float cs = col_ok ? g.colscale[col] : 0.0f;
+    for (int jn = 0; jn < OUT_FRAGS; ++jn)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (col_ok && row < e.M) {
-            const int hi = acc[i][jn][r], lo = acc[i][jn + 2][r];
-            if (g.acc_hi) {
-              g.acc_hi[row * e.N + col] = hi;
-              g.acc_lo[row * e.N + col] = lo;
-            } else {
-              const double t = 128.0 * (double)hi + (double)lo;
-              store_out(e, row, col, (float)t * g.a_s[row] * cs);
-            }
+          const int64_t row = wave_row0 + i * 32 + (r >> 2) * 8 + lrow + (r & 3);
+          const int64_t col = wave_col0 + jn * 32 + lcol;
+          if (row < e.M && col < e.N) {
+            g.acc_hi[row * e.N + col] = acc[i][jn][r];
+            g.acc_lo[row * e.N + col] = acc[i][jn + OUT_FRAGS][r];
           }
         }
-    }
-  } else {
-    const float alpha = (*g.a_ts) * (*g.w_ts);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = nb0 + wn * 128 + j * 32 + (lane & 31);
-      const bool col_ok = col < e.N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (col_ok && row < e.M) store_out(e, row, col, acc[i][j][r] * alpha);
-        }
-    }
+    return;
   }
+  float* ep = reinterpret_cast<float*>(smem) + wave * (C::EP_FM * 32 * kEpiStride);
+  const float alpha = I8 ? 1.0f : (*g.a_ts) * (*g.w_ts);
+#pragma unroll
+  for (int ip = 0; ip < C::FM; ip += C::EP_FM)
+#pragma unroll
+    for (int jp = 0; jp < OUT_FRAGS; jp += 2) {
+#pragma unroll
+      for (int i = 0; i < C::EP_FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float v;
+            if constexpr (I8)
+              v = fmaf(128.0f, (float)acc[ip + i][jp + jj][r],
+                       (float)acc[ip + i][jp + jj + OUT_FRAGS][r]);
+            else
+              v = acc[ip + i][jp + jj][r] * alpha;
+            ep[(i * 32 + (r >> 2) * 8 + lrow + (r & 3)) * kEpiStride + jj * 32 + lcol] = v;
+          }
+      __syncthreads();
+      for (int it = 0; it < C::EP_FM * 8; ++it) {
+        const int idx = it * 64 + lane;
+        const int rl = idx >> 4, c4 = (idx & 15) * 4;
+        const int64_t row = wave_row0 + ip * 32 + rl;
+        const int64_t col = wave_col0 + jp * 32 + c4;
+        if (row >= e.M || col >= e.N) continue;
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(ep + rl * kEpiStride + c4);
+        float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+        const float rs = I8 ? g.a_s[row] : 1.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (I8 && col + q < e.N) v[q] = v[q] * rs * g.colscale[col + q];
+          if (e.bias && col + q < e.N) v[q] += __uint_as_float((uint32_t)e.bias[col + q] << 16);
+          if (e.gelu) v[q] = gelu_tanh(v[q]);
+        }
+        const bool full = col + 4 <= e.N && e.vec_ok;
+        if (e.out_f32) {
+          float* yp = static_cast<float*>(e.y) + row * e.ldy + col;
+          if (full)
+            *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+          else
+            for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = v[q];
+        } else {
+          uint16_t* yp = static_cast<uint16_t*>(e.y) + row * e.ldy + col;
+          if (full) {
+            u32x2 o = {f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                       f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+            *reinterpret_cast<u32x2*>(yp) = o;
+          } else {
+            for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = (uint16_t)f32_to_bf16(v[q]);
+          }
+        }
+      }
+      __syncthreads();
+    }
 }
 
 // Exact INT8 x NVFP4 columns for irregular weight rows: per 16-group integer
-// sums scaled by the group's E4M3 value in float64.
+// sums scaled by the group's E4M3 value in float64.  Each workgroup scans
+// 256 row flags at once (one per thread) and then walks the flagged rows
+// in index order; with no irregular rows it only reads the flags.
 __global__ void __launch_bounds__(256)
 int8_irregular_kernel(const int8_t* __restrict__ a_q, const float* __restrict__ a_s,
                       const uint8_t* __restrict__ w_q, const uint8_t* __restrict__ w_s,
                       const float* __restrict__ w_ts, int64_t K,
                       const uint8_t* __restrict__ irregular, EpiArgs e) {
+  __shared__ uint64_t masks[4];
   const int64_t gpr = K / 16;
-  for (int64_t n = blockIdx.x; n < e.N; n += gridDim.x) {
-    if (!irregular[n]) continue;
-    for (int64_t m = threadIdx.x; m < e.M; m += blockDim.x) {
-      double acc = 0.0;
-      for (int64_t gi = 0; gi < gpr; ++gi) {
-        const u32x2 c = *reinterpret_cast<const u32x2*>(w_q + n * (K / 2) + gi * 8);
-        const int8_t* qa = a_q + m * K + gi * 16;
-        int p = 0;
+  const int wave = threadIdx.x >> 6;
+  for (int64_t nb = (int64_t)blockIdx.x * 256; nb < e.N; nb += (int64_t)gridDim.x * 256) {
+    const int64_t mine = nb + threadIdx.x;
+    const bool flag = mine < e.N && irregular[mine] != 0;
+    const uint64_t bal = __ballot(flag);
+    if ((threadIdx.x & 63) == 0) masks[wave] = bal;
+    __syncthreads();
+    for (int w = 0; w < 4; ++w) {
+      uint64_t bits = masks[w];
+      while (bits) {
+        const int bit = __ffsll((unsigned long long)bits) - 1;
+        bits &= bits - 1;
+        const int64_t n = nb + w * 64 + bit;
+        for (int64_t m = threadIdx.x; m < e.M; m += blockDim.x) {
+          double acc = 0.0;
+          for (int64_t gi = 0; gi < gpr; ++gi) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(w_q + n * (K / 2) + gi * 8);
+            const int8_t* qa = a_q + m * K + gi * 16;
+            int p = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          p += (int)qa[i] * e2m1_twice((c[i >> 3] >> (4 * (i & 7))) & 0xFu);
-        acc += (double)p * (double)e4m3_decode(w_s[n * gpr + gi]);
+            for (int i = 0; i < 16; ++i)
+              p += (int)qa[i] * e2m1_twice((c[i >> 3] >> (4 * (i & 7))) & 0xFu);
+            acc += (double)p * (double)e4m3_decode(w_s[n * gpr + gi]);
+          }
+          store_out(e, m, n, (float)(acc * 0.5 * (double)a_s[m] * (double)(*w_ts)));
+        }
       }
-      store_out(e, m, n, (float)(acc * 0.5 * (double)a_s[m] * (double)(*w_ts)));
     }
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- host --
+
+static int vec_ok(const GemmOut& o) {
+  return (reinterpret_cast<uintptr_t>(o.y) % 16 == 0) && (o.ldy % 4 == 0);
+}
 
 static int64_t kpad_bytes(int64_t k_bytes) { return round_up(k_bytes, kRowBytes); }
 
@@ -396,6 +523,10 @@ void set_gemm_events(hipEvent_t before, hipEvent_t after) {
   g_ev_after = after;
 }
 
+#ifndef QACT_BF16_WN
+#define QACT_BF16_WN 2
+#endif
+
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
   const int total = g.mt * g.nt;
   const int grid = 8 * ((total + 7) / 8);
@@ -403,10 +534,14 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
     hipError_t err = hipEventRecord(g_ev_before, st);
     if (err != hipSuccess) return err;
   }
-  if (i8)
-    hipLaunchKernelGGL(qgemm_kernel<true>, dim3(grid), dim3(kThreads), 0, st, g, e);
+  constexpr int kWnBf16 = QACT_BF16_WN;
+  if (i8 && g.acc_hi)
+    hipLaunchKernelGGL((qgemm_kernel<true, true, 2>), dim3(grid), dim3(Cfg<2>::NT), 0, st, g, e);
+  else if (i8)
+    hipLaunchKernelGGL((qgemm_kernel<true, false, 2>), dim3(grid), dim3(Cfg<2>::NT), 0, st, g, e);
   else
-    hipLaunchKernelGGL(qgemm_kernel<false>, dim3(grid), dim3(kThreads), 0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<false, false, kWnBf16>), dim3(grid), dim3(Cfg<kWnBf16>::NT),
+                       0, st, g, e);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && g_ev_after) err = hipEventRecord(g_ev_after, st);
   return err;
@@ -444,7 +579,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
   g.nt = (int)(np / 256);
   g.a_ts = a_ts;
   g.w_ts = w_ts;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
   return launch_gemm(false, g, e, st);
 }
 
@@ -475,11 +610,12 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
   g.colscale = colscale;
   g.acc_hi = acc_hi;
   g.acc_lo = acc_lo;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
   err = launch_gemm(true, g, e, st);
   if (err != hipSuccess || acc_hi) return err;
-  hipLaunchKernelGGL(int8_irregular_kernel, dim3(64), dim3(256), 0, st, a_q, a_s, w_q, w_s, w_ts,
-                     K, irregular, e);
+  const int64_t fb = (N + 255) / 256;
+  hipLaunchKernelGGL(int8_irregular_kernel, dim3((unsigned)(fb < 1024 ? fb : 1024)), dim3(256), 0,
+                     st, a_q, a_s, w_q, w_s, w_ts, K, irregular, e);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ namespace qact {
 
 static constexpr int kRedBlocks = 2048;
 static constexpr int kThreads = 256;
+static constexpr int kUnroll = 4;
 
 enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2 };
 
@@ -58,20 +59,36 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
            double* __restrict__ partial, int want_sums) {
   Acc4 a = {{0.0, 0.0, 0.0, 0.0}};
   const int64_t nvec = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
-    const u32x4 xv = reinterpret_cast<const u32x4*>(in)[v];
-    const u32x4 bv = reinterpret_cast<const u32x4*>(b)[v];
-    u32x4 pv = {0, 0, 0, 0};
-    if (PREV) pv = reinterpret_cast<const u32x4*>(prev)[v];
-    u32x4 ov;
+  // kUnroll vectors per thread and sweep: all loads issued before any use
+  const int64_t sweep = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t v0 = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; v0 < nvec;
+       v0 += sweep) {
+    u32x4 xv[kUnroll], bv[kUnroll], pv[kUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = tdc_pair<MODE, PREV>(xv[i] & 0xFFFFu, bv[i] & 0xFFFFu, pv[i] & 0xFFFFu, a);
-      const uint32_t hi = tdc_pair<MODE, PREV>(xv[i] >> 16, bv[i] >> 16, pv[i] >> 16, a);
-      ov[i] = lo | (hi << 16);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kThreads;
+      if (v < nvec) {
+        xv[u] = reinterpret_cast<const u32x4*>(in)[v];
+        bv[u] = reinterpret_cast<const u32x4*>(b)[v];
+        pv[u] = PREV ? reinterpret_cast<const u32x4*>(prev)[v] : u32x4{0, 0, 0, 0};
+      } else {
+        xv[u] = bv[u] = pv[u] = u32x4{0, 0, 0, 0};
+      }
     }
-    if (MODE != MODE_GAMMA) reinterpret_cast<u32x4*>(dst)[v] = ov;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kThreads;
+      u32x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = tdc_pair<MODE, PREV>(xv[u][i] & 0xFFFFu, bv[u][i] & 0xFFFFu,
+                                                 pv[u][i] & 0xFFFFu, a);
+        const uint32_t hi = tdc_pair<MODE, PREV>(xv[u][i] >> 16, bv[u][i] >> 16, pv[u][i] >> 16, a);
+        ov[i] = lo | (hi << 16);
+      }
+      if (MODE != MODE_GAMMA && v < nvec)
+        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst) + v);
+    }
   }
   // ragged tail (n % 8 elements), done by workgroup 0
   if (blockIdx.x == 0) {
@@ -98,23 +115,31 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
 }
 
 // Fixed-order sum of the per-workgroup rows: thread t adds rows t, t+256,
-// ... of each column, then the waves combine in order.
+// ... (all four columns, loads issued together), then the waves combine in
+// order.
 __global__ void __launch_bounds__(kThreads)
 tdc_finalize_kernel(const double* __restrict__ partial, int rows, int ncols,
                     double* __restrict__ sums) {
   __shared__ double red[4][kThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int r = threadIdx.x; r < rows; r += kThreads) {
+    const double4 p = reinterpret_cast<const double4*>(partial)[r];
+    s[0] += p.x;
+    s[1] += p.y;
+    s[2] += p.z;
+    s[3] += p.w;
+  }
+#pragma unroll
   for (int j = 0; j < 4; ++j) {
-    double s = 0.0;
-    for (int r = threadIdx.x; r < rows; r += kThreads) s += partial[(int64_t)r * 4 + j];
-    s = wave_sum(s);
-    if (lane == 0) red[j][wave] = s;
+    const double t = wave_sum(s[j]);
+    if (lane == 0) red[j][wave] = t;
   }
   __syncthreads();
   if (threadIdx.x < ncols) {
-    double s = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) s += red[threadIdx.x][w];
-    sums[threadIdx.x] = s;
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) t += red[threadIdx.x][w];
+    sums[threadIdx.x] = t;
   }
 }
 
@@ -123,7 +148,7 @@ size_t reduce_ws_bytes(int64_t) { return (size_t)kRedBlocks * 4 * sizeof(double)
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* prev,
                       uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream) {
   const int64_t nvec = n / 8;
-  int64_t nb = (nvec + kThreads - 1) / kThreads;
+  int64_t nb = (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   if (nb > kRedBlocks) nb = kRedBlocks;
   if (nb < 1) nb = 1;
   double* partial = static_cast<double*>(ws);
