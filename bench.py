@@ -18,6 +18,7 @@ by the library's event hook, so their time excludes operand preparation.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -56,6 +57,25 @@ class Hip:
         self.h.hipEventDestroy(e)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (two
+    rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by the same
+    counters on a plain device copy of known size), or None when the file
+    is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "mixed_precision_quantized_act_amd", "csrc", rec["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(x, w, x_out, delta_prev, rows):
     """The oracle, untuned, on the first `rows` token rows of the workload."""
     import numpy as np
@@ -91,8 +111,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -185,6 +207,12 @@ def main():
         qa.tdc_decide(t, [d], [1], 0.05)
         return pairs
 
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for t in range(args.warmup):
         step(False, t)
     torch.cuda.synchronize()
@@ -241,7 +269,8 @@ def main():
     else:
         dom, ach, peak, dt = "gemm_nvfp4", tf(avg["gemm_nvfp4"]), PEAK["bf16_TFLOPs"], "bf16"
     roofline = {"bound": "mfma", "kernel": dom, "dtype": dt, "achieved": round(ach, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom)}
 
     line = {
         "metric": "qlinear TFLOP/s (NVFP4 & INT8 A-paths) + quant/TDC GB/s, % of roofline",

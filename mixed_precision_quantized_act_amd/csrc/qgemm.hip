@@ -15,17 +15,20 @@
 //    integer I = c M 2^(F-Fr) (c = 2*E2M1, scale = M 2^(F-10)), split into
 //    two int8 digit planes I = 128 hi + lo; both planes run against the
 //    int8 activations on v_mfma_i32_32x32x32_i8 with exact int32 sums,
-//    combined in float64 per output.  Rows whose scale exponents spread by
-//    more than 6 (never for Gaussian weights) are computed by a separate
-//    exact kernel.
+//    combined per output.  Rows whose scale exponents spread by more than 6
+//    (never for Gaussian weights) are computed by a separate exact kernel.
 //
-// Tiling (both paths): 256 threads = 4 waves in a 2x2 grid, a 256 x 256
-// output tile (INT8: 256 x 128 columns times 2 digit planes), K stages of
-// 128 bytes per row (64 bf16 or 128 int8) double-buffered in LDS (2 x 64
-// KB), rows stored with a 16-byte-chunk XOR swizzle so that the 16-byte
-// fragment reads of 32 consecutive rows hit distinct banks.  Each wave owns
-// a 128 x 128 block of accumulators (16 MFMA tiles of 32 x 32).  Workgroups
-// are remapped so each XCD works a contiguous band of tiles (L2 reuse).
+// Tiling (both paths): a workgroup of 4 waves (2 x 2) computes a 256 x 128
+// tile of B rows (NVFP4: 128 output columns; INT8: 64 output columns in
+// each of the two digit planes); each wave owns 128 x 64 as 4 x 2 MFMA
+// tiles of 32 x 32.  K advances in stages of 64 bytes per row (32 bf16 or
+// 64 int8), loaded straight from global memory into a 3-deep LDS ring
+// (24 KB per stage) by buffer loads whose out-of-range lanes return zero
+// (ragged M and K of the unpadded INT8 activations).  With 72 KB of LDS
+// and at most 256 registers per lane, two workgroups share a CU, so one
+// workgroup's barriers, prologue and epilogue run under the other's
+// MFMAs.  Workgroups are remapped so each XCD works a contiguous band of
+// tiles (L2 reuse).
 #include <type_traits>
 
 #include "qact_device.h"
@@ -39,13 +42,19 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(16))) int i32x16;
 
-static constexpr int kTileM = 256;
-static constexpr int kTileRowsB = 256;        // B tile rows per stage (bf16: N; int8: 2 x 128)
-static constexpr int kRowBytes = 128;         // bytes per tile row per K stage
-static constexpr int kStageBytes = (kTileM + kTileRowsB) * kRowBytes;
+static constexpr int kThreads = 256;          // 4 waves, 2 x 2
+static constexpr int kTileM = 256;            // A rows per tile
+static constexpr int kTileB = 128;            // B rows per tile (INT8: 2 planes x 64)
+static constexpr int kRowBytes = 64;          // bytes per tile row per K stage
+static constexpr int kStageBytes = (kTileM + kTileB) * kRowBytes;   // 24 KB
+static constexpr int kStages = 3;             // LDS ring depth: 2 stages in flight
 static constexpr int kGroupM = 8;
+static constexpr int kFM = 4, kFN = 2;        // MFMA tiles per wave (rows, B columns)
 static constexpr int kEpiStride = 72;         // floats per staged output row
-static constexpr int kSmemBytes = 4 * 128 * kEpiStride * 4;   // >= 2 operand stages
+static constexpr int kEpiBytes = 4 * 32 * kEpiStride * 4;          // 32 rows per wave per pass
+static constexpr int kScaleFloats = 128 + 32;                      // INT8: row + column scales
+static constexpr int kRingBytes = kStages * kStageBytes;
+static constexpr int kSmemBytes = kRingBytes + 4 * kScaleFloats * 4;
 
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -173,7 +182,7 @@ __device__ __forceinline__ void store_out(const EpiArgs& e, int64_t row, int64_t
 struct GemmArgs {
   const uint8_t* A;      // rows of kRowBytes-aligned K bytes
   int64_t lda;           // bytes
-  int64_t a_rows;        // rows that exist (loads clamp to a_rows - 1)
+  int64_t a_rows;        // rows that exist (the buffer range ends there)
   int64_t a_kbytes;      // K bytes that exist (later chunks load as 0)
   const uint8_t* B;
   int64_t ldb;           // bytes
@@ -189,40 +198,12 @@ struct GemmArgs {
   int32_t* acc_lo;
 };
 
-// Wave grid of a workgroup: WM x WN waves (WM = 2).  A wave owns a
-// (256/WM) x (256/WN) block of the 256 x 256 output tile (INT8: (256/WM) x
-// (128/WN) columns of each of the two digit planes), as FM x FN MFMA tiles
-// of 32 x 32.
-template <int WN>
-struct Cfg {
-  static constexpr int WM = 2;
-  static constexpr int NW = WM * WN;              // waves
-  static constexpr int NT = 64 * NW;              // threads
-  static constexpr int FM = 256 / WM / 32;        // A fragments per wave
-  static constexpr int FN = 256 / WN / 32;        // B fragments per wave
-  static constexpr int RPP = NT / 8;              // tile rows per staging pass
-  static constexpr int PASSES = 256 / RPP;        // staging passes per operand
-  static constexpr int EP_FM = NW == 4 ? 4 : 2;   // A fragments per epilogue pass
-};
-
-template <bool I8, int WN>
-__device__ __forceinline__ int b_frag_row(int wn, int j, int lane) {
-  constexpr int FN = Cfg<WN>::FN;
-  if (I8) {
-    constexpr int half = FN / 2;                  // column fragments per digit plane
-    return (j / half) * 128 + wn * (128 / WN) + (j % half) * 32 + (lane & 31);
-  }
-  return wn * (256 / WN) + j * 32 + (lane & 31);
-}
-
-// LDS swizzle: 16-byte chunk c of tile row r sits in chunk slot
-// c ^ ((r >> 1) & 7) of its 128-byte row.  A 16-lane group of a 16-byte
-// fragment read covers 16 consecutive rows at one chunk: even rows land in
-// one half of the 64 banks and odd rows in the other, and (r >> 1) & 7
-// spreads each half's 8 rows over the 8 slots, so the group hits 64
-// distinct banks.  The staging writes (8 lanes per row) are conflict-free
-// too.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// LDS swizzle: 16-byte chunk c of a 64-byte tile row r sits in slot
+// c ^ ((r >> 2) & 3).  A 16-lane group of a 16-byte fragment read covers 16
+// consecutive rows at one chunk; 4 rows fill the 64 banks and (r >> 2) & 3
+// moves each row quartet to different slots, so the group hits 64 distinct
+// banks.  The direct-to-LDS loads write each wave's 1 KB lane-linearly.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   // raw buffer (stride 0): loads at offsets >= bytes return zero
@@ -230,16 +211,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16 * l (the LDS address is wave-uniform and goes through M0).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds,
+                                                  uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
 }
 
-template <bool I8, bool DUMP, int WN>
-__global__ void __launch_bounds__(Cfg<WN>::NT, 1)
+// Wait until at most n vector-memory operations of this wave are in flight.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// B-tile row of MFMA fragment j of wave column wn (lane's row inside it is
+// lane % 32).  INT8: fragment 0 is the hi plane, 1 the lo plane, same columns.
+template <bool I8>
+__device__ __forceinline__ int b_frag_row(int wn, int j) {
+  if (I8) return j * 64 + wn * 32;
+  return wn * 64 + j * 32;
+}
+
+template <bool I8, bool DUMP>
+__global__ void __launch_bounds__(kThreads, 2)
 qgemm_kernel(GemmArgs g, EpiArgs e) {
-  using C = Cfg<WN>;
-  static_assert(kSmemBytes >= 2 * kStageBytes, "LDS holds two operand stages");
-  static_assert(C::NW * C::EP_FM * 32 * kEpiStride * 4 <= kSmemBytes, "epilogue staging fits");
+  static_assert(kEpiBytes <= kRingBytes, "epilogue staging reuses the ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
 
   // XCD-aware tile order: hardware deals workgroups to the 8 XCDs in turn;
@@ -256,10 +254,10 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   const int tm = first_m + in_group % gsz;
   const int tn = in_group / gsz;
   const int64_t m0 = (int64_t)tm * kTileM;
-  const int64_t nb0 = (int64_t)tn * (I8 ? 128 : 256);
+  const int64_t nb0 = (int64_t)tn * (I8 ? kTileB / 2 : kTileB);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
 
   // Buffer resources based at this tile's first row: rows past the operand
   // (INT8 activations: rows >= M) fall outside the range and load zero.
@@ -268,70 +266,67 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   const __amdgpu_buffer_rsrc_t ra_src = buffer_rsrc(g.A + m0 * g.lda, (uint32_t)a_bytes);
   const __amdgpu_buffer_rsrc_t rb_src = buffer_rsrc(g.B + nb0 * g.ldb, 0x7FFFFFF0u);
 
-  // global -> register staging: per K stage each thread moves PASSES chunks
-  // of 16 bytes of A and of B; chunk i covers tile row i*RPP + tid/8, byte
-  // column (tid%8)*16 (RPP is a multiple of 16, so every chunk of a thread
-  // has the same swizzle).
-  const int r8 = tid >> 3, ch8 = tid & 7;
-  const int lds_base = r8 * kRowBytes + ((ch8 ^ swz(r8)) << 4);
-  const uint32_t a_off = (uint32_t)(r8 * g.lda + ch8 * 16);
-  const uint32_t a_step = (uint32_t)(C::RPP * g.lda);
-  const uint32_t b_off = (uint32_t)(r8 * g.ldb + ch8 * 16);
-  u32x4 ra[C::PASSES], rb[C::PASSES];
-  auto gload = [&](int kt) {
+  // Direct-to-LDS staging.  A stage holds 256 A rows then 128 B rows of 64
+  // bytes; one wave instruction fills 16 rows (1 KB): lane l takes row l/4
+  // of its 16 and the chunk that belongs in slot l%4 of that row.  The 16 A
+  // groups and 8 B groups of a stage are spread over the 4 waves.
+  constexpr int kAGroups = kTileM / 16 / 4, kBGroups = kTileB / 16 / 4;   // per wave
+  const int ld_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t lane_a = (uint32_t)((lane >> 2) * g.lda + ld_chunk * 16);
+  const uint32_t lane_b = (uint32_t)((lane >> 2) * g.ldb + ld_chunk * 16);
+  auto issue = [&](int kt, int buf) {
+    uint8_t* sbase = smem + buf * kStageBytes;
     const uint32_t kb = (uint32_t)kt * kRowBytes;
     // the INT8 activation rows are unpadded: a chunk past K loads zero
-    const bool kin = !I8 || (int64_t)kb + ch8 * 16 < g.a_kbytes;
+    const bool kin = !I8 || (int64_t)kb + ld_chunk * 16 < g.a_kbytes;
 #pragma unroll
-    for (int i = 0; i < C::PASSES; ++i) {
-      ra[i] = buffer_load16(ra_src, kin ? a_off + i * a_step + kb : 0x7FFFFFF0u);
-      const int trow = i * C::RPP;                // first tile row of this pass
-      const uint32_t bo = I8 ? (uint32_t)(trow / 128) * (uint32_t)g.b_plane +
-                                   (uint32_t)((trow % 128) * g.ldb)
-                             : (uint32_t)(trow * g.ldb);
-      rb[i] = buffer_load16(rb_src, b_off + bo + kb);
+    for (int i = 0; i < kAGroups; ++i) {
+      const int grp = i * 4 + wave;                // 16-row group of A, 0..15
+      const uint32_t ao = (uint32_t)(grp * 16) * (uint32_t)g.lda + lane_a + kb;
+      buffer_load_lds16(ra_src, sbase + grp * 1024, kin ? ao : 0x7FFFFFF0u);
     }
-  };
-  auto lds_store = [&](int buf) {
-    uint8_t* sa = smem + buf * kStageBytes + lds_base;
-    uint8_t* sb = sa + kTileM * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < C::PASSES; ++i) {
-      *reinterpret_cast<u32x4*>(sa + i * C::RPP * kRowBytes) = ra[i];
-      *reinterpret_cast<u32x4*>(sb + i * C::RPP * kRowBytes) = rb[i];
+    for (int i = 0; i < kBGroups; ++i) {
+      const int grp = i * 4 + wave;                // 16-row group of B, 0..7
+      const int trow = grp * 16;
+      const uint32_t bo = I8 ? (uint32_t)(trow / 64) * (uint32_t)g.b_plane +
+                                   (uint32_t)(trow % 64) * (uint32_t)g.ldb
+                             : (uint32_t)trow * (uint32_t)g.ldb;
+      buffer_load_lds16(rb_src, sbase + kTileM * kRowBytes + grp * 1024, bo + lane_b + kb);
     }
   };
 
   typedef typename std::conditional<I8, i32x16, f32x16>::type acc_t;
-  acc_t acc[C::FM][C::FN];
+  acc_t acc[kFM][kFN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+    for (int j = 0; j < kFN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   // fragment rows of this lane are (multiple of 32) + lane % 32, so they
   // all share the swizzle of lane % 32
-  const int a_frag = (wm * (256 / C::WM) + (lane & 31)) * kRowBytes;
+  const int a_frag = (wm * 128 + (lane & 31)) * kRowBytes;
+  const int b_frag = (lane & 31) * kRowBytes;
   const int row_sw = swz(lane & 31);
-  auto frags = [&](int buf, int s, u32x4 (&af)[C::FM], u32x4 (&bf)[C::FN]) {
+  auto frags = [&](int buf, int s, u32x4 (&af)[kFM], u32x4 (&bf)[kFN]) {
     const uint8_t* sa = smem + buf * kStageBytes;
     const uint8_t* sb = sa + kTileM * kRowBytes;
     const int coff = ((2 * s + (lane >> 5)) ^ row_sw) << 4;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < kFM; ++i)
       af[i] = *reinterpret_cast<const u32x4*>(sa + a_frag + i * 32 * kRowBytes + coff);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(sb + b_frag_row<I8, WN>(wn, j, lane) * kRowBytes +
+    for (int j = 0; j < kFN; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(sb + b_frag + b_frag_row<I8>(wn, j) * kRowBytes +
                                               coff);
   };
-  auto mfmas = [&](const u32x4 (&af)[C::FM], const u32x4 (&bf)[C::FN]) {
+  auto mfmas = [&](const u32x4 (&af)[kFM], const u32x4 (&bf)[kFN]) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
+      for (int j = 0; j < kFN; ++j) {
         if constexpr (I8)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, af[i]),
                                                             __builtin_bit_cast(i32x4, bf[j]),
@@ -343,116 +338,123 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       }
   };
 
-  // Pipeline: LDS holds stage kt while registers carry stage kt+1 from
-  // global memory; fragments of substep s+1 are read while the MFMAs of
-  // substep s run.  At substep 3 the next stage goes to the other LDS
-  // buffer (one barrier per stage) and the loads of stage kt+2 are issued.
-  gload(0);
-  lds_store(0);
-  __syncthreads();
-  if (g.k_tiles > 1) gload(1);
-  u32x4 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
-  frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < g.k_tiles; ++kt) {
-    const int cur = kt & 1;
-    frags(cur, 1, fa1, fb1);
+  // Pipeline over the LDS ring: stages kt+1 and kt+2 are in flight while
+  // stage kt is multiplied.  Before stage kt is read, each wave waits for
+  // its own loads of stage kt (the loads of the younger stage may stay
+  // outstanding) and a barrier makes every wave's loads visible; the same
+  // barrier guarantees that stage kt-1's buffer, which the loads of stage
+  // kt+2 overwrite, is no longer read.
+  constexpr int kLoadsPerStage = kAGroups + kBGroups;
+  const int nk = g.k_tiles;
+  for (int p = 0; p < kStages - 1 && p < nk; ++p) issue(p, p);
+  u32x4 fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
+  int buf = 0, nbuf = kStages - 1;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk)
+      wait_vm<kLoadsPerStage>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, nbuf);
+    frags(buf, 0, fa0, fb0);
+    frags(buf, 1, fa1, fb1);
     mfmas(fa0, fb0);
-    frags(cur, 2, fa0, fb0);
     mfmas(fa1, fb1);
-    frags(cur, 3, fa1, fb1);
-    mfmas(fa0, fb0);
-    if (kt + 1 < g.k_tiles) {
-      lds_store(cur ^ 1);
-      __syncthreads();
-      frags(cur ^ 1, 0, fa0, fb0);
-      if (kt + 2 < g.k_tiles) gload(kt + 2);
-    }
-    mfmas(fa1, fb1);
+    buf = buf + 1 == kStages ? 0 : buf + 1;
+    nbuf = nbuf + 1 == kStages ? 0 : nbuf + 1;
   }
 
   // ---- epilogue.  Accumulator r of a 32x32 MFMA tile holds row
-  // (r/4)*8 + (lane/32)*4 + r%4 and column lane%32.  In passes of EP_FM row
-  // fragments x 64 columns, each wave stages its values as float32 in LDS
-  // (row stride kEpiStride floats: the two half-waves write disjoint
-  // banks), then reads them back row-contiguous and stores 4 consecutive
-  // outputs per lane.
-  __syncthreads();                       // every wave is done with the operand tiles
+  // (r/4)*8 + (lane/32)*4 + r%4 and column lane%32.  In passes of 32 rows,
+  // each wave stages its values as float32 in LDS (row stride kEpiStride
+  // floats: the two half-waves write disjoint banks), then reads them back
+  // row-contiguous and stores 4 consecutive outputs per lane.
+  __syncthreads();                       // every wave is done with the operand ring
   const int lrow = (lane >> 5) * 4, lcol = lane & 31;
-  constexpr int OUT_FRAGS = I8 ? C::FN / 2 : C::FN;     // 32-column output blocks per wave
-  const int64_t wave_row0 = m0 + wm * (256 / C::WM);
-  const int64_t wave_col0 = nb0 + wn * (OUT_FRAGS * 32);
+  constexpr int kOutCols = I8 ? 32 : 64;           // output columns per wave
+  const int64_t wave_row0 = m0 + wm * 128;
+  const int64_t wave_col0 = nb0 + wn * kOutCols;
   if constexpr (I8 && DUMP) {          // verification dump of the exact sums
 #pragma unroll
-    for (int jn = 0; jn < OUT_FRAGS; ++jn)
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = wave_row0 + i * 32 + (r >> 2) * 8 + lrow + (r & 3);
-          const int64_t col = wave_col0 + jn * 32 + lcol;
-          if (row < e.M && col < e.N) {
-            g.acc_hi[row * e.N + col] = acc[i][jn][r];
-            g.acc_lo[row * e.N + col] = acc[i][jn + OUT_FRAGS][r];
-          }
-        }
-    return;
-  }
-  float* ep = reinterpret_cast<float*>(smem) + wave * (C::EP_FM * 32 * kEpiStride);
-  const float alpha = I8 ? 1.0f : (*g.a_ts) * (*g.w_ts);
-#pragma unroll
-  for (int ip = 0; ip < C::FM; ip += C::EP_FM)
-#pragma unroll
-    for (int jp = 0; jp < OUT_FRAGS; jp += 2) {
-#pragma unroll
-      for (int i = 0; i < C::EP_FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float v;
-            if constexpr (I8)
-              v = fmaf(128.0f, (float)acc[ip + i][jp + jj][r],
-                       (float)acc[ip + i][jp + jj + OUT_FRAGS][r]);
-            else
-              v = acc[ip + i][jp + jj][r] * alpha;
-            ep[(i * 32 + (r >> 2) * 8 + lrow + (r & 3)) * kEpiStride + jj * 32 + lcol] = v;
-          }
-      __syncthreads();
-      for (int it = 0; it < C::EP_FM * 8; ++it) {
-        const int idx = it * 64 + lane;
-        const int rl = idx >> 4, c4 = (idx & 15) * 4;
-        const int64_t row = wave_row0 + ip * 32 + rl;
-        const int64_t col = wave_col0 + jp * 32 + c4;
-        if (row >= e.M || col >= e.N) continue;
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(ep + rl * kEpiStride + c4);
-        float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-        const float rs = I8 ? g.a_s[row] : 1.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (I8 && col + q < e.N) v[q] = v[q] * rs * g.colscale[col + q];
-          if (e.bias && col + q < e.N) v[q] += __uint_as_float((uint32_t)e.bias[col + q] << 16);
-          if (e.gelu) v[q] = gelu_tanh(v[q]);
-        }
-        const bool full = col + 4 <= e.N && e.vec_ok;
-        if (e.out_f32) {
-          float* yp = static_cast<float*>(e.y) + row * e.ldy + col;
-          if (full)
-            *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
-          else
-            for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = v[q];
-        } else {
-          uint16_t* yp = static_cast<uint16_t*>(e.y) + row * e.ldy + col;
-          if (full) {
-            u32x2 o = {f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
-                       f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
-            *reinterpret_cast<u32x2*>(yp) = o;
-          } else {
-            for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = (uint16_t)f32_to_bf16(v[q]);
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = wave_row0 + i * 32 + (r >> 2) * 8 + lrow + (r & 3);
+        const int64_t col = wave_col0 + lcol;
+        if (row < e.M && col < e.N) {
+          g.acc_hi[row * e.N + col] = acc[i][0][r];
+          g.acc_lo[row * e.N + col] = acc[i][1][r];
         }
       }
-      __syncthreads();
+    return;
+  }
+  float* ep = reinterpret_cast<float*>(smem) + wave * (32 * kEpiStride);
+  const float alpha = I8 ? 1.0f : (*g.a_ts) * (*g.w_ts);
+  // INT8: the wave's row scales (s_a) and column scales (s_Tw 2^(Fr-11))
+  // go to LDS once, so the store loop reads no scale from global memory
+  float* sc_row = reinterpret_cast<float*>(smem + kRingBytes) + wave * kScaleFloats;
+  float* sc_col = sc_row + 128;
+  if constexpr (I8) {
+    for (int i = lane; i < 128; i += 64) {
+      const int64_t row = wave_row0 + i;
+      sc_row[i] = row < e.M ? g.a_s[row] : 0.0f;
     }
+    if (lane < 32) {
+      const int64_t col = wave_col0 + lane;
+      sc_col[lane] = col < e.N ? g.colscale[col] : 0.0f;
+    }
+  }
+  constexpr int kLanesPerRow = kOutCols / 4;       // 4 outputs per lane
+  constexpr int kRowsPerIter = 64 / kLanesPerRow;
+#pragma unroll
+  for (int ip = 0; ip < kFM; ++ip) {
+#pragma unroll
+    for (int jj = 0; jj < kOutCols / 32; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v;
+        if constexpr (I8)
+          v = fmaf(128.0f, (float)acc[ip][0][r], (float)acc[ip][1][r]);
+        else
+          v = acc[ip][jj][r] * alpha;
+        ep[((r >> 2) * 8 + lrow + (r & 3)) * kEpiStride + jj * 32 + lcol] = v;
+      }
+    __syncthreads();
+    for (int it = 0; it < 32 / kRowsPerIter; ++it) {
+      const int rl = it * kRowsPerIter + lane / kLanesPerRow;
+      const int c4 = (lane % kLanesPerRow) * 4;
+      const int64_t row = wave_row0 + ip * 32 + rl;
+      const int64_t col = wave_col0 + c4;
+      if (row >= e.M || col >= e.N) continue;
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(ep + rl * kEpiStride + c4);
+      float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+      const float rs = I8 ? sc_row[ip * 32 + rl] : 1.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (I8) v[q] = v[q] * rs * sc_col[c4 + q];
+        if (e.bias && col + q < e.N) v[q] += __uint_as_float((uint32_t)e.bias[col + q] << 16);
+        if (e.gelu) v[q] = gelu_tanh(v[q]);
+      }
+      const bool full = col + 4 <= e.N && e.vec_ok;
+      if (e.out_f32) {
+        float* yp = static_cast<float*>(e.y) + row * e.ldy + col;
+        if (full)
+          *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+        else
+          for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = v[q];
+      } else {
+        uint16_t* yp = static_cast<uint16_t*>(e.y) + row * e.ldy + col;
+        if (full) {
+          u32x2 o = {f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                     f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+          *reinterpret_cast<u32x2*>(yp) = o;
+        } else {
+          for (int q = 0; q < 4 && col + q < e.N; ++q) yp[q] = (uint16_t)f32_to_bf16(v[q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Exact INT8 x NVFP4 columns for irregular weight rows: per 16-group integer
@@ -508,11 +510,12 @@ static int64_t kpad_bytes(int64_t k_bytes) { return round_up(k_bytes, kRowBytes)
 
 size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t kp = kpad_bytes(2 * K) / 2;
-  return (size_t)round_up(round_up(M, 256) * kp * 2, 256) + (size_t)round_up(N, 256) * kp * 2;
+  return (size_t)round_up(round_up(M, kTileM) * kp * 2, 256) +
+         (size_t)round_up(N, kTileB) * kp * 2;
 }
 
 size_t int8_gemm_ws_bytes(int64_t, int64_t N, int64_t K) {
-  const int64_t kp = kpad_bytes(K), np = round_up(N, 128);
+  const int64_t kp = kpad_bytes(K), np = round_up(N, kTileB / 2);
   return (size_t)round_up(2 * np * kp, 256) + (size_t)round_up(np * 4, 256) + (size_t)np;
 }
 
@@ -523,10 +526,6 @@ void set_gemm_events(hipEvent_t before, hipEvent_t after) {
   g_ev_after = after;
 }
 
-#ifndef QACT_BF16_WN
-#define QACT_BF16_WN 2
-#endif
-
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
   const int total = g.mt * g.nt;
   const int grid = 8 * ((total + 7) / 8);
@@ -534,14 +533,12 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
     hipError_t err = hipEventRecord(g_ev_before, st);
     if (err != hipSuccess) return err;
   }
-  constexpr int kWnBf16 = QACT_BF16_WN;
   if (i8 && g.acc_hi)
-    hipLaunchKernelGGL((qgemm_kernel<true, true, 2>), dim3(grid), dim3(Cfg<2>::NT), 0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, g, e);
   else if (i8)
-    hipLaunchKernelGGL((qgemm_kernel<true, false, 2>), dim3(grid), dim3(Cfg<2>::NT), 0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<true, false>), dim3(grid), dim3(kThreads), 0, st, g, e);
   else
-    hipLaunchKernelGGL((qgemm_kernel<false, false, kWnBf16>), dim3(grid), dim3(Cfg<kWnBf16>::NT),
-                       0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<false, false>), dim3(grid), dim3(kThreads), 0, st, g, e);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && g_ev_after) err = hipEventRecord(g_ev_after, st);
   return err;
@@ -552,9 +549,10 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
                              int64_t M, int64_t N, int64_t K, const GemmOut& o, void* ws,
                              hipStream_t st) {
   const int64_t kp = kpad_bytes(2 * K) / 2;
-  const int64_t mp = round_up(M, 256), np = round_up(N, 256);
+  const int64_t mp = round_up(M, kTileM), np = round_up(N, kTileB);
   uint16_t* a_bf = static_cast<uint16_t*>(ws);
-  uint16_t* w_bf = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + round_up(mp * kp * 2, 256));
+  uint16_t* w_bf =
+      reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + round_up(mp * kp * 2, 256));
   auto grid_for = [](int64_t groups) {
     int64_t b = (groups + 255) / 256;
     return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
@@ -575,8 +573,8 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
   g.B = reinterpret_cast<const uint8_t*>(w_bf);
   g.ldb = kp * 2;
   g.k_tiles = (int)(kp * 2 / kRowBytes);
-  g.mt = (int)(mp / 256);
-  g.nt = (int)(np / 256);
+  g.mt = (int)(mp / kTileM);
+  g.nt = (int)(np / kTileB);
   g.a_ts = a_ts;
   g.w_ts = w_ts;
   EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
@@ -587,9 +585,10 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
                             const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
                             int64_t K, const GemmOut& o, int32_t* acc_hi, int32_t* acc_lo,
                             void* ws, hipStream_t st) {
-  const int64_t kp = kpad_bytes(K), np = round_up(N, 128);
+  const int64_t kp = kpad_bytes(K), np = round_up(N, kTileB / 2);
   int8_t* planes = static_cast<int8_t*>(ws);
-  float* colscale = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + round_up(2 * np * kp, 256));
+  float* colscale =
+      reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + round_up(2 * np * kp, 256));
   uint8_t* irregular = reinterpret_cast<uint8_t*>(colscale) + round_up(np * 4, 256);
   hipLaunchKernelGGL(nvfp4_to_int8_digits_kernel, dim3((unsigned)((np + 3) / 4)), dim3(256), 0,
                      st, w_q, w_s, w_ts, N, K, np, kp, planes, colscale, irregular);
@@ -604,8 +603,8 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
   g.ldb = kp;
   g.b_plane = np * kp;
   g.k_tiles = (int)(kp / kRowBytes);
-  g.mt = (int)((M + 255) / 256);
-  g.nt = (int)(np / 128);
+  g.mt = (int)((M + kTileM - 1) / kTileM);
+  g.nt = (int)(np / (kTileB / 2));
   g.a_s = a_s;
   g.colscale = colscale;
   g.acc_hi = acc_hi;

@@ -37,7 +37,18 @@ from .formats import bf16_to_f64, f64_to_bf16_rne
 
 
 def _fsum(a):
+    """Correctly rounded float64 sum."""
     return math.fsum(np.asarray(a, dtype=np.float64).ravel().tolist())
+
+
+def _psum(a):
+    """Pairwise float64 sum (numpy): for n non-negative terms its relative
+    error is below ceil(log2 n) * 2^-53 (about 3e-15 for n = 2^25), used
+    where the correctly rounded sum is too slow (whole DiT stacks)."""
+    return float(np.sum(np.asarray(a, dtype=np.float64)))
+
+
+_SUM = {"exact": _fsum, "pairwise": _psum}
 
 
 def ratio(num, den):
@@ -47,11 +58,13 @@ def ratio(num, den):
     return num / den
 
 
-def gamma_sums(in_bits, out_bits):
-    """(S1, S2) = (sum|out - in|, sum|in|), each correctly rounded."""
+def gamma_sums(in_bits, out_bits, summation="exact"):
+    """(S1, S2) = (sum|out - in|, sum|in|), each correctly rounded (or
+    pairwise, see _psum)."""
     x = bf16_to_f64(in_bits)
     y = bf16_to_f64(out_bits)
-    return _fsum(np.abs(y - x)), _fsum(np.abs(x))
+    add = _SUM[summation]
+    return add(np.abs(y - x)), add(np.abs(x))
 
 
 def gamma(in_bits, out_bits):
@@ -60,21 +73,22 @@ def gamma(in_bits, out_bits):
     return ratio(s1, s2)
 
 
-def tdc_update(in_bits, out_bits, delta_prev_bits=None):
+def tdc_update(in_bits, out_bits, delta_prev_bits=None, summation="exact"):
     """Delta_new = bf16(out - in) and the sums S1..S4.
 
     S1 = sum|out - in|, S2 = sum|in|, S3 = sum (Delta_new - Delta_prev)^2,
     S4 = sum Delta_prev^2; S3 = S4 = 0 without a previous Delta.
     """
+    add = _SUM[summation]
     x = bf16_to_f64(in_bits)
     y = bf16_to_f64(out_bits)
     delta_new = f64_to_bf16_rne(y - x)
-    s1, s2 = _fsum(np.abs(y - x)), _fsum(np.abs(x))
+    s1, s2 = add(np.abs(y - x)), add(np.abs(x))
     if delta_prev_bits is None:
         return delta_new, (s1, s2, 0.0, 0.0)
     dn = bf16_to_f64(delta_new)
     dp = bf16_to_f64(delta_prev_bits)
-    return delta_new, (s1, s2, _fsum((dn - dp) ** 2), _fsum(dp ** 2))
+    return delta_new, (s1, s2, add((dn - dp) ** 2), add(dp ** 2))
 
 
 def rel_l2(s3, s4):
@@ -133,7 +147,8 @@ def tdc_decide(t, d_prev, computed_prev, delta):
 class BlockCache:
     """TDC state of one block: two-slot Delta ring, flags and the last d."""
 
-    def __init__(self):
+    def __init__(self, summation="exact"):
+        self.summation = summation
         self.ring = [None, None]
         self.last = 1            # the first Delta goes to slot 0
         self.n_stored = 0
@@ -150,7 +165,7 @@ class BlockCache:
 
     def computed(self, in_bits, out_bits):
         """A computed step: store the new Delta, record d; returns sums."""
-        delta_new, sums = tdc_update(in_bits, out_bits, self.delta_last())
+        delta_new, sums = tdc_update(in_bits, out_bits, self.delta_last(), self.summation)
         d = rel_l2(sums[2], sums[3]) if self.n_stored else math.inf
         self.last ^= 1
         self.ring[self.last] = delta_new

@@ -156,3 +156,15 @@ def test_fp32_then_bf16_equals_exact_rounding():
     exact = T.tdc_update(a, b)[0]
     np.testing.assert_array_equal(via32, exact)
     np.testing.assert_array_equal(F.f32_to_bf16_rne((fa + fb).astype(np.float32)), T.tdc_apply(a, b))
+
+
+def test_pairwise_sums_within_bound():
+    rng = np.random.default_rng(9)
+    x = _bf16(rng.standard_normal(1 << 20))
+    y = _bf16(F.bf16_to_f64(x) + 0.05 * rng.standard_normal(1 << 20))
+    p = rng.standard_normal(1 << 20)
+    pb = _bf16(p)
+    _, exact = T.tdc_update(x, y, pb)
+    _, pair = T.tdc_update(x, y, pb, summation="pairwise")
+    for a, b in zip(exact, pair):
+        assert abs(a - b) <= 21 * 2.0 ** -53 * abs(a)
