@@ -208,11 +208,15 @@ def main():
         return pairs
 
     if args.calib_copy:
-        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        # a 256 MiB device copy whose source was written and then evicted
+        # from the caches by reading 2 GiB of other data
+        src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        flush = torch.ones(1 << 29, dtype=torch.int32, device=dev)
+        flush.sum()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
     for t in range(args.warmup):
         step(False, t)
     torch.cuda.synchronize()

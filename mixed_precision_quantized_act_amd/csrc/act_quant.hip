@@ -19,11 +19,7 @@ namespace qact {
 static constexpr int kUnroll = 4;
 
 __device__ __forceinline__ uint32_t abs_max8(u32x4 a, uint32_t mx) {
-  // max of the |bf16| bit patterns of 8 packed values (ordered like the
-  // magnitudes, since the patterns of non-negative floats sort as integers)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mx = max(mx, max(a[i] & 0x7FFFu, (a[i] >> 16) & 0x7FFFu));
-  return mx;
+  return max(mx, fold_max(abs_max8_pk(a, u16x2{0, 0})));
 }
 
 __device__ __forceinline__ void block_max_to(float v, float* dst) {
@@ -103,17 +99,10 @@ nvfp4_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_
     u32x2 codes[G];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      const uint32_t mx = abs_max8(w[2 * gg + 1], abs_max8(w[2 * gg], 0u));
+      const uint32_t mx = fold_max(abs_max8_pk(w[2 * gg + 1], abs_max8_pk(w[2 * gg], u16x2{0, 0})));
       const uint32_t enc = e4m3_encode(__uint_as_float(mx << 16) * g);
       const float inv = recip0(e4m3_decode(enc) * s_t);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wa = w[2 * gg][i], wb = w[2 * gg + 1][i];
-        lo |= (e2m1_encode(bf16_lo(wa) * inv) | (e2m1_encode(bf16_hi(wa) * inv) << 4)) << (8 * i);
-        hi |= (e2m1_encode(bf16_lo(wb) * inv) | (e2m1_encode(bf16_hi(wb) * inv) << 4)) << (8 * i);
-      }
-      codes[gg] = u32x2{lo, hi};
+      codes[gg] = u32x2{e2m1_pack8(w[2 * gg], inv), e2m1_pack8(w[2 * gg + 1], inv)};
       sc_word |= enc << (8 * gg);
     }
     uint8_t* qp = q + row * (K / 2) + (int64_t)c * 8 * G;

@@ -45,17 +45,36 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 code of a float32 value: nearest of 0,.5,1,1.5,2,3,4,6 with ties to
-// the even code, saturating; bit 3 = the sign bit of v.  Each decision
-// threshold sits on a tie, which belongs to the even code: 0|1 at .25 (>),
-// 1|2 at .75 (>=), 2|3 at 1.25 (>), 3|4 at 1.75 (>=), 4|5 at 2.5 (>),
-// 5|6 at 3.5 (>=), 6|7 at 5 (>).
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  float a = fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// E2M1 codes of two float32 values, packed into byte `sel` of `old` (the
+// first value in the low nibble): nearest of 0,.5,1,1.5,2,3,4,6 with ties
+// to the even code, saturating at 6, bit 3 = the sign bit of the input.
+// gfx950's v_cvt_scalef32_pk_fp4_f32 with a unit scale rounds exactly so
+// (checked against the threshold rule on every finite float32).
+#define QACT_E2M1_PK(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// E2M1 codes of the 8 bf16 values of a 16-byte vector times `inv`, as 8
+// nibbles (element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t e2m1_pack8(u32x4 w, float inv) {
+  uint32_t r = 0;
+  r = QACT_E2M1_PK(r, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, 0);
+  r = QACT_E2M1_PK(r, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv, 1);
+  r = QACT_E2M1_PK(r, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, 2);
+  r = QACT_E2M1_PK(r, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv, 3);
+  return r;
 }
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+// Max of the |bf16| bit patterns of the 8 values in a 16-byte vector,
+// folded into mx (the patterns of non-negative floats sort as integers);
+// two values per packed 16-bit max.
+__device__ __forceinline__ u16x2 abs_max8_pk(u32x4 a, u16x2 mx) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, a[i] & 0x7FFF7FFFu));
+  return mx;
+}
+__device__ __forceinline__ uint32_t fold_max(u16x2 m) { return max((uint32_t)m[0], (uint32_t)m[1]); }
 
 // E2M1 value times 2 (an integer in -12..12) of a 4-bit code.
 __device__ __forceinline__ int e2m1_twice(uint32_t c) {

@@ -17,9 +17,15 @@
 
 namespace qact {
 
-static constexpr int kRedBlocks = 2048;
+#ifndef QACT_TDC_UNROLL
+#define QACT_TDC_UNROLL 4
+#endif
+#ifndef QACT_TDC_BLOCKS
+#define QACT_TDC_BLOCKS 2048
+#endif
+static constexpr int kRedBlocks = QACT_TDC_BLOCKS;
 static constexpr int kThreads = 256;
-static constexpr int kUnroll = 4;
+static constexpr int kUnroll = QACT_TDC_UNROLL;
 
 enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2 };
 
@@ -44,10 +50,12 @@ __device__ __forceinline__ uint32_t tdc_pair(uint32_t xi, uint32_t bi, uint32_t 
   if (MODE == MODE_GAMMA) return 0;
   const uint32_t dn = f32_to_bf16(b - x);
   if (PREV) {
+    // fused multiply-add: each square joins the sum with one rounding (the
+    // square of a short bf16 difference is exact in float64 anyway)
     const double p = (double)__uint_as_float(pi << 16);
     const double diff = (double)__uint_as_float(dn << 16) - p;
-    a.s[2] += diff * diff;
-    a.s[3] += p * p;
+    a.s[2] = __fma_rn(diff, diff, a.s[2]);
+    a.s[3] = __fma_rn(p, p, a.s[3]);
   }
   return dn;
 }
