@@ -101,10 +101,16 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  * W NVFP4 [N][K] (w_q, w_s, w_ts).  bias: bf16 [N] or NULL.
  * y: bf16 or f32 [M][ldy], ldy >= N.  epi: QA_EPI_GELU_TANH applies
  * 0.5 v (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))) after the bias.
- * Accuracy: relative Frobenius error against the exact (float64) product
- * rounded to the output type is far below 1e-3; the NVFP4 path multiplies
- * exactly dequantized operands with float32 accumulation; the INT8 path
- * forms exact int32 sums (see qlinear_int8_acc) and scales them in float.
+ * Accuracy: both paths multiply exactly dequantized operands (each NVFP4
+ * value E2M1 x E4M3 and each int8 is exact in fp16; the tensor scales and
+ * the INT8 row scales are applied to the float32 sums), so an output
+ * differs from the exact (float64) product by the float32 accumulation
+ * over K -- about K 2^-24 times sum_k |a_k w_k| at worst -- plus the final
+ * rounding to the output type; the relative Frobenius error is far below
+ * 1e-3.
+ * Workspace: qlinear_workspace() bytes (a per-tile copy of the E4M3 scales
+ * of the operands, about (M + N) K / 16 bytes), device memory that the
+ * call may overwrite.
  * y must not overlap any input.  Requires 0 < K, K % 16 == 0, M, N >= 0.
  * ------------------------------------------------------------------------ */
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
@@ -118,21 +124,6 @@ int qlinear_int8(const int8_t* a_q, const float* a_s,
                  int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                  void* y, int64_t ldy, qa_out out, qa_epi epi,
                  void* ws, size_t ws_bytes, hipStream_t stream);
-
-/* The INT8 path's exact integer sums, for verification.  Each NVFP4 weight
- * row n is written W[n][k] = s_Tw 2^(Fr[n]-11) I[n][k] with an integer I:
- * an E4M3 scale is M 2^(F-10) (normal: M = 8 + mantissa, F = exponent
- * field; subnormal: M = mantissa, F = 1), an E2M1 value is c/2 with
- * c in {0,1,2,3,4,6,8,12}, Fr[n] = the row's smallest F over scales with
- * M > 0, and I = c M 2^(F - Fr[n]).  Rows whose F spread exceeds 6 are
- * "irregular"; the others split I = 128 hi + lo, lo in [-64, 63].
- * acc_hi/acc_lo: int32 [M][N], the exact sums over k of q[m][k] * hi[n][k]
- * and q[m][k] * lo[n][k]; columns of irregular rows are written as 0.
- * Uses the qlinear_workspace(QA_INT8, ...) scratch. */
-int qlinear_int8_acc(const int8_t* a_q, const uint8_t* w_q, const uint8_t* w_s,
-                     int64_t M, int64_t N, int64_t K,
-                     int32_t* acc_hi, int32_t* acc_lo,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* act_quant of x followed by the matching qlinear_* (one layer).  For
  * NVFP4 the tensor scale is computed from x (flags may hold

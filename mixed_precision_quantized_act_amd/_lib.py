@@ -39,7 +39,6 @@ _SIGS = {
                                      ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
     "qlinear_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                     ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
-    "qlinear_int8_acc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "qlinear_layer_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _I64, _I64,
                                _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
@@ -137,12 +136,6 @@ def qlinear_int8(a_q, a_s, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, 
     _check("qlinear_int8", lib().qlinear_int8(
         _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), _ptr(y),
         ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
-
-
-def qlinear_int8_acc(a_q, w_q, w_s, acc_hi, acc_lo, M, N, K, ws=None, stream=None):
-    _check("qlinear_int8_acc", lib().qlinear_int8_acc(
-        _ptr(a_q), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(acc_hi), _ptr(acc_lo), _ptr(ws),
-        _nbytes(ws), _stream(stream)))
 
 
 def qlinear_layer_workspace(fmt, M, N, K):

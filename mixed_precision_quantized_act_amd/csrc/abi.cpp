@@ -121,7 +121,10 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
   if (!a_q || !a_s || !a_ts || !w_q || !w_s || !w_ts) return QA_EINVAL;
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
-  if (ws_bytes < nvfp4_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
+  {
+    const size_t need = nvfp4_gemm_ws_bytes(M, N, K);
+    if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
+  }
   if (!aligned16(ws)) return QA_EALIGN;
   const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * (out == QA_OUT_F32 ? 4 : 2) : 0;
   if (overlap(y, ybytes, a_q, (size_t)(M * K / 2)) || overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
@@ -139,7 +142,10 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
   if (!a_q || !a_s || !w_q || !w_s || !w_ts) return QA_EINVAL;
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
-  if (ws_bytes < int8_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
+  {
+    const size_t need = int8_gemm_ws_bytes(M, N, K);
+    if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
+  }
   if (!aligned16(ws)) return QA_EALIGN;
   const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * (out == QA_OUT_F32 ? 4 : 2) : 0;
   if (overlap(y, ybytes, a_q, (size_t)(M * K)) || overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
@@ -148,22 +154,7 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
   return hip_status(
-      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, nullptr, nullptr, ws, stream));
-}
-
-int qlinear_int8_acc(const int8_t* a_q, const uint8_t* w_q, const uint8_t* w_s, int64_t M,
-                     int64_t N, int64_t K, int32_t* acc_hi, int32_t* acc_lo, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
-  if (!a_q || !w_q || !w_s || !acc_hi || !acc_lo) return QA_EINVAL;
-  if (int s = check_mk(M, K)) return s;
-  if (N < 0 || N >= kMaxDim) return QA_ESHAPE;
-  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
-  if (ws_bytes < int8_gemm_ws_bytes(M, N, K) || !ws) return QA_EWORKSPACE;
-  if (M == 0 || N == 0) return QA_OK;
-  // the dump needs no tensor or activation scales (w_ts = null)
-  GemmOut o = {nullptr, 0, 0, 0, nullptr};
-  return hip_status(launch_int8_gemm(a_q, nullptr, w_q, w_s, nullptr, M, N, K, o, acc_hi, acc_lo,
-                                     ws, stream));
+      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, stream));
 }
 
 size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {

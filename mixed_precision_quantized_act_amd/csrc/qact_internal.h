@@ -34,8 +34,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
 size_t int8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
                             const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
-                            int64_t K, const GemmOut& o, int32_t* acc_hi, int32_t* acc_lo,
-                            void* ws, hipStream_t stream);
+                            int64_t K, const GemmOut& o, void* ws, hipStream_t stream);
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 size_t reduce_ws_bytes(int64_t n);

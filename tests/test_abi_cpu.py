@@ -68,8 +68,12 @@ def test_qlinear_validation():
     assert _status("qlinear_nvfp4", None, *ok[1:], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, big, None) == -1
     assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
     assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900001), 4, 0, 0, FAKE, big, None) == -3
-    assert qa.qlinear_workspace(qa.NVFP4, 17776, 5760, 1920) > 17776 * 1920 * 2
-    assert qa.qlinear_workspace(qa.INT8, 17776, 5760, 1920) >= 2 * 5760 * 1920
+    # per-tile copies of the E4M3 scales: 4 bytes per row and K unit of 64,
+    # rows rounded up to tiles of 256
+    units = (1920 + 63) // 64
+    tiles = lambda r: (r + 255) // 256
+    assert qa.qlinear_workspace(qa.NVFP4, 17776, 5760, 1920) >= (tiles(17776) + tiles(5760)) * units * 1024
+    assert qa.qlinear_workspace(qa.INT8, 17776, 5760, 1920) == tiles(5760) * units * 1024
 
 
 def test_tdc_validation():

@@ -1,7 +1,10 @@
 """GPU parity of the quantized linears.  Outputs: relative Frobenius error
 <= 1e-3 against the float64 oracle rounded to the output type (the
-tolerance the method's checker states); INT8 integer accumulators: bit
-exact.  Operands are quantized by the oracle, so the GEMM is isolated."""
+tolerance the method's checker states); float32 outputs also element by
+element within the float32-accumulation bound (K + 3) 2^-24 sum_k |a_k w_k|
+of exactly dequantized operands, and bit-exact where every partial sum is
+exact in float32.  Operands are quantized by the oracle, so the GEMM is
+isolated."""
 import numpy as np
 import pytest
 
@@ -57,24 +60,14 @@ def run_int8(a, w, M, N, K, bias=None, out_f32=False, gelu=False):
     return _out_host(y, out_f32)
 
 
-def run_int8_acc(q, w, M, N, K):
-    qa, t = _qa(), torch()
-    hi = t.empty((M, N), dtype=t.int32, device="cuda")
-    lo = t.empty((M, N), dtype=t.int32, device="cuda")
-    ws = qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K))
-    qa.qlinear_int8_acc(dev(q), dev(w[0]), dev(w[1]), hi, lo, M, N, K, ws=ws)
-    t.cuda.synchronize()
-    return host(hi), host(lo)
-
-
 def _case(M, N, K, seed, dist="normal"):
     x = synth.activations(seed, M, K, dist, min(4, K // 16), 20.0 if dist == "normal" else 1.0)
     w = synth.weight(seed, 0, N, K)
     return x, w
 
 
-SHAPES = [(256, 256, 256), (1, 16, 16), (300, 200, 48), (257, 300, 80), (64, 5760, 1920),
-          (130, 7680, 1920), (70, 1920, 7680)]
+SHAPES = [(256, 256, 256), (1, 16, 16), (300, 200, 48), (257, 300, 80), (77, 90, 112),
+          (513, 257, 96), (64, 5760, 1920), (130, 7680, 1920), (70, 1920, 7680)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -97,15 +90,31 @@ def test_int8_linear(M, N, K, out_f32):
     assert rel_fro(y, _round_ref(ref, out_f32)) <= TOL
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 48), (130, 640, 1920), (33, 96, 7680)])
-def test_int8_accumulators_exact(M, N, K):
+def _elementwise_bound(a_deq, w_deq, K):
+    # float32 accumulation of K exact products, then at most two float32
+    # scalings: |y - exact| <= (K + 3) 2^-24 sum_k |a_k w_k|
+    return (K + 3) * 2.0 ** -24 * (np.abs(a_deq) @ np.abs(w_deq).T) + 1e-300
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 48), (130, 640, 1920),
+                                   (33, 96, 7680)])
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+def test_f32_output_elementwise_bound(M, N, K, path):
     x, w = _case(M, N, K, seed=13)
-    q, _ = Q.int8_encode(x)
     wq = Q.nvfp4_encode(w)
-    hi, lo = run_int8_acc(q, wq, M, N, K)
-    ohi, olo = G.int8_accumulators(q, wq[0], wq[1])
-    np.testing.assert_array_equal(hi, ohi)
-    np.testing.assert_array_equal(lo, olo)
+    wd = Q.nvfp4_decode(*wq)
+    if path == "nvfp4":
+        a = Q.nvfp4_encode(x)
+        ad = Q.nvfp4_decode(*a)
+        y = run_nvfp4(a, wq, M, N, K, out_f32=True)
+    else:
+        a = Q.int8_encode(x)
+        ad = Q.int8_decode(*a)
+        y = run_int8(a, wq, M, N, K, out_f32=True)
+    ref = G.linear_ref(ad, wd)
+    err = np.abs(y - ref)
+    bound = _elementwise_bound(ad, wd, K)
+    assert np.all(err <= bound), float(np.max(err / bound))
 
 
 @pytest.mark.parametrize("path", ["nvfp4", "int8"])
@@ -125,23 +134,46 @@ def test_bias_and_gelu(path):
     assert rel_fro(y, _round_ref(ref, False)) <= TOL
 
 
-def test_int8_irregular_weight_rows():
-    # rows whose group scales spread over more than 2^6 take the exact
-    # per-group path; the others take the digit-plane GEMM
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+def test_wide_scale_spread_rows(path):
+    # weight rows whose group scales spread over many binades (a group
+    # 1e3-1e4 times smaller than the rest of its row)
     M, N, K = 96, 64, 128
     x, w = _case(M, N, K, seed=15)
     wf = F.bf16_to_f64(w)
     wf[3, :16] *= 1e-3
     wf[40, 32:48] *= 1e-4
     w = F.f64_to_bf16_rne(wf)
-    a, wq = Q.int8_encode(x), Q.nvfp4_encode(w)
-    _, _, regular = G.weight_integer_repr(wq[0], wq[1])
-    assert not regular[3] and not regular[40]
-    ref = G.linear_ref(Q.int8_decode(*a), Q.nvfp4_decode(*wq))
+    wq = Q.nvfp4_encode(w)
+    wd = Q.nvfp4_decode(*wq)
+    if path == "nvfp4":
+        a = Q.nvfp4_encode(x)
+        ad = Q.nvfp4_decode(*a)
+        run = lambda out_f32: run_nvfp4(a, wq, M, N, K, out_f32=out_f32)
+    else:
+        a = Q.int8_encode(x)
+        ad = Q.int8_decode(*a)
+        run = lambda out_f32: run_int8(a, wq, M, N, K, out_f32=out_f32)
+    ref = G.linear_ref(ad, wd)
     for out_f32 in (False, True):
-        y = run_int8(a, wq, M, N, K, out_f32=out_f32)
+        y = run(out_f32)
         assert rel_fro(y, _round_ref(ref, out_f32)) <= TOL
         assert rel_fro(y[:, [3, 40]], _round_ref(ref[:, [3, 40]], out_f32)) <= TOL
+    assert np.all(np.abs(y - ref) <= _elementwise_bound(ad, wd, K))
+
+
+def test_int8_small_integers_exact_f32():
+    # unit weight scales, power-of-two tensor and row scales: every partial
+    # sum is a multiple of 1/2 below 2^24, exact in float32
+    M, N, K = 96, 80, 192
+    rng = np.random.default_rng(5)
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    s_a = np.float32(2.0) ** rng.integers(-4, 4, M).astype(np.float32)
+    w = (rng.integers(0, 256, (N, K // 2), dtype=np.uint8),
+         np.full((N, K // 16), 0x38, np.uint8), np.float32(0.125))
+    ref = G.linear_ref(Q.int8_decode(q, s_a), Q.nvfp4_decode(*w))
+    y = run_int8((q, s_a), w, M, N, K, out_f32=True)
+    np.testing.assert_array_equal(y, ref)
 
 
 def test_power_of_two_scales_exact_f32():
