@@ -57,7 +57,16 @@ static constexpr int kRowBytes = 64;            // fp16 bytes per tile row per s
 static constexpr int kF16Stage = kTileM * kRowBytes;   // A only: 16 KB
 static constexpr int kF16Bufs = 3;
 static constexpr int kRawSlots = 4;
-static constexpr int kGroupM = 8;
+#ifndef QACT_GROUP_M
+#define QACT_GROUP_M 8
+#endif
+#ifndef QACT_VALU_PER_MFMA
+#define QACT_VALU_PER_MFMA 3
+#endif
+#ifndef QACT_COMPUTE_PRIO
+#define QACT_COMPUTE_PRIO 0
+#endif
+static constexpr int kGroupM = QACT_GROUP_M;
 static constexpr int kFM = 4, kFN = 2;          // MFMA tiles per wave (rows, columns)
 
 // One raw unit in LDS: A codes, B codes, A scale words, B scale words.
@@ -84,26 +93,26 @@ static inline int64_t units_of(int64_t K) { return (K + kUnitK - 1) / kUnitK; }
 // scale bytes of each row as one word: dst[(tile * units + u) * 256 + r].
 // Rows past `rows` and groups past K/16 read as 0 (a zero scale makes the
 // corresponding fp16 values zero, whatever codes the raw unit holds there).
+// One workgroup per (tile, unit), one thread per row.
 __global__ void __launch_bounds__(256)
-scale_tiles_kernel(const uint8_t* __restrict__ s, int64_t rows, int64_t K, int64_t tiles,
-                   int64_t units, uint32_t* __restrict__ dst) {
+scale_tiles_kernel(const uint8_t* __restrict__ s, int64_t rows, int64_t K, int units,
+                   uint32_t* __restrict__ dst) {
+  const int tu = (int)blockIdx.x;
+  const int u = tu % units, t = tu / units;
+  const int64_t row = (int64_t)t * 256 + threadIdx.x;
   const int64_t gpr = K / 16;
-  const int64_t total = tiles * units * 256;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i & 255, tu = i >> 8;
-    const int64_t u = tu % units, t = tu / units;
-    const int64_t row = t * 256 + r;
-    uint32_t v = 0;
-    if (row < rows) {
+  uint32_t v = 0;
+  if (row < rows) {
+    const uint8_t* p = s + row * gpr + 4 * u;
+    if ((gpr & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 3) == 0 && 4 * (int64_t)u + 4 <= gpr) {
+      v = *reinterpret_cast<const uint32_t*>(p);
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t g = 4 * u + j;
-        if (g < gpr) v |= (uint32_t)s[row * gpr + g] << (8 * j);
-      }
+      for (int j = 0; j < 4; ++j)
+        if (4 * (int64_t)u + j < gpr) v |= (uint32_t)p[j] << (8 * j);
     }
-    dst[i] = v;
   }
+  dst[(int64_t)tu * 256 + threadIdx.x] = v;
 }
 
 // ------------------------------------------------------------ epilogue --
@@ -474,6 +483,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     RawA rap = ra;
     pin(rbp.w[0]); pin(rbp.w[1]); pin(rbp.sw[0]); pin(rbp.sw[1]);
     pin(rap.a); pin(rap.as);
+    if (QACT_COMPUTE_PRIO) __builtin_amdgcn_s_setprio(QACT_COMPUTE_PRIO);
     mfmas(fa0, b0);
     mfmas(fa1, b1);
     conv_b(kt + 1, rbp, n0, n1);
@@ -481,7 +491,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
 #pragma unroll
     for (int i = 0; i < 2 * kFM * kFN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, QACT_VALU_PER_MFMA, 0);   // VALU
     }
     __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // DS writes
     // the W fragments of stage kt+1 are complete here (not sunk into the
@@ -491,6 +501,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       pin(n0[j]);
       pin(n1[j]);
     }
+    if (QACT_COMPUTE_PRIO) __builtin_amdgcn_s_setprio(0);
     wait_lds();
     barrier();
   };
@@ -615,12 +626,8 @@ void set_gemm_events(hipEvent_t before, hipEvent_t after) {
 static hipError_t launch_scale_tiles(const uint8_t* s, int64_t rows, int64_t K, uint32_t* dst,
                                      hipStream_t st) {
   const int64_t tiles = (rows + kTileM - 1) / kTileM, units = units_of(K);
-  const int64_t total = tiles * units * 256;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s, rows, K,
-                     tiles, units, dst);
+  hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)(tiles * units)), dim3(256), 0, st, s, rows,
+                     K, (int)units, dst);
   return hipGetLastError();
 }
 
