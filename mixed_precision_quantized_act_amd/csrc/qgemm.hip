@@ -551,22 +551,25 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
           float v[4];
           epi_vals(i, j, q, rs, v);
           *reinterpret_cast<u32x2*>(stg + c * 128 + (((4 * j + q) ^ (c & 7)) << 4) + 8 * lh) =
-              u32x2{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
-                    f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+              u32x2{bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3])};
         }
       wait_lds();
+      // this pass's 32 x 64 block: rows below e.M - prow0, columns below
+      // e.N - wave_col0 exist
+      const int64_t prow0 = wave_row0 + i * 32;
+      uint16_t* const ybase = static_cast<uint16_t*>(e.y) + prow0 * e.ldy + wave_col0;
+      const int64_t rows_left = e.M - prow0, cols_left = e.N - wave_col0;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3), k = lane & 7;
         const u32x4 d = *reinterpret_cast<const u32x4*>(stg + r * 128 + ((k ^ (r & 7)) << 4));
-        const int64_t row = wave_row0 + i * 32 + r;
-        const int64_t col = wave_col0 + k * 8;
-        if (row < e.M && col < e.N) {
-          uint16_t* yp = static_cast<uint16_t*>(e.y) + row * e.ldy + col;
-          if (col + 8 <= e.N)
+        if (r < rows_left && k * 8 < cols_left) {
+          uint16_t* yp = ybase + (int64_t)r * e.ldy + k * 8;
+          if (k * 8 + 8 <= cols_left)
             *reinterpret_cast<u32x4*>(yp) = d;
           else
-            for (int t = 0; col + t < e.N; ++t) yp[t] = (uint16_t)(d[t >> 1] >> (16 * (t & 1)));
+            for (int t = 0; k * 8 + t < cols_left; ++t)
+              yp[t] = (uint16_t)(d[t >> 1] >> (16 * (t & 1)));
         }
       }
       wait_lds();
@@ -593,7 +596,9 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
               for (int t = 0; t < 4 && col + t < e.N; ++t) yp[t] = v[t];
           } else {
             uint16_t* yp = static_cast<uint16_t*>(e.y) + row * e.ldy + col;
-            for (int t = 0; t < 4 && col + t < e.N; ++t) yp[t] = (uint16_t)f32_to_bf16(v[t]);
+            const uint32_t p01 = bf16_pack(v[0], v[1]), p23 = bf16_pack(v[2], v[3]);
+            const uint32_t pk[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+            for (int t = 0; t < 4 && col + t < e.N; ++t) yp[t] = (uint16_t)pk[t];
           }
         }
     }
