@@ -231,3 +231,42 @@ def test_ffn_full_shape_sampled_rows(path):
     y = run(a2, wdn, M, K, F_)
     ref2 = G.linear_ref(dec(a2, rows), Q.nvfp4_decode(*wdn))
     assert rel_fro(y[rows], _round_ref(ref2, False)) <= TOL
+
+
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_strided_output_bias_gelu(path, out_f32):
+    # y is a column window of a wider buffer (ldy > N; for bf16 the window
+    # starts at a 16-byte boundary, for the second case it does not), with
+    # bias and GELU; the columns outside the window must stay untouched
+    qa, t = _qa(), torch()
+    M, N, K = 300, 200, 192
+    x, w = _case(M, N, K, seed=16)
+    bias = F.f64_to_bf16_rne(np.random.default_rng(1).standard_normal(N))
+    wq = Q.nvfp4_encode(w)
+    if path == "nvfp4":
+        a = Q.nvfp4_encode(x)
+        ref = G.linear_ref(Q.nvfp4_decode(*a), Q.nvfp4_decode(*wq), bias, gelu=True)
+    else:
+        a = Q.int8_encode(x)
+        ref = G.linear_ref(Q.int8_decode(*a), Q.nvfp4_decode(*wq), bias, gelu=True)
+    dt = t.float32 if out_f32 else t.bfloat16
+    for off in (8, 3):
+        ldy = N + 24
+        big = t.full((M, ldy), -7.0, dtype=dt, device="cuda")
+        y = big[:, off:off + N]
+        ws = qa.workspace(qa.qlinear_workspace(qa.NVFP4 if path == "nvfp4" else qa.INT8, M, N, K))
+        out = qa.OUT_F32 if out_f32 else qa.OUT_BF16
+        if path == "nvfp4":
+            qa.qlinear_nvfp4(dev(a[0]), dev(a[1]), dev(np.array([a[2]], np.float32)), dev(wq[0]),
+                             dev(wq[1]), dev(np.array([wq[2]], np.float32)), y, M, N, K,
+                             bias=dev(bias), out=out, epi=qa.EPI_GELU_TANH, ws=ws, ldy=ldy)
+        else:
+            qa.qlinear_int8(dev(a[0]), dev(a[1]), dev(wq[0]), dev(wq[1]),
+                            dev(np.array([wq[2]], np.float32)), y, M, N, K, bias=dev(bias),
+                            out=out, epi=qa.EPI_GELU_TANH, ws=ws, ldy=ldy)
+        t.cuda.synchronize()
+        got = _out_host(y.contiguous(), out_f32)
+        assert rel_fro(got, _round_ref(ref, out_f32)) <= TOL
+        rest = t.cat([big[:, :off], big[:, off + N:]], dim=1).float().cpu().numpy()
+        assert np.all(rest == -7.0)
