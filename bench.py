@@ -12,9 +12,11 @@ One step is one pass of the whole hot path over that batch:
   tdc_apply (the skip path, with Gamma sums) ;
   copy of the sums to the host, dmpq_mask and tdc_decide.
 `value` is the linear FLOPs of both activation paths per second of whole
-steps (2 * 2*M*N*K per step).  Per-kernel times come from HIP events on
-the launch stream inside the timed steps; the GEMM kernels are bracketed
-by the library's event hook, so their time excludes operand preparation.
+steps (2 * 2*M*N*K per step).  The GEMM kernel times come from HIP events
+that the library's hook attaches to the GEMM dispatches themselves inside
+the timed steps (their start and end timestamps, on the launch stream);
+the times of the other calls come from event markers around each library
+call in as many extra, untimed steps after the timed region.
 """
 import argparse
 import ctypes
@@ -165,47 +167,51 @@ def main():
 
     names = ["act_quant_nvfp4", "qlinear_nvfp4", "gemm_nvfp4", "act_quant_int8", "qlinear_int8",
              "gemm_int8", "tdc_update", "tdc_apply"]
-    ev = {k: [] for k in names}
+    host_np = host_sums.numpy()
+    gamma_buf = np.zeros(1, np.float64)
+    d_buf = np.zeros(1, np.float64)
+    computed = np.ones(1, np.uint8)
+    mask_out = np.zeros(4, np.uint8)
+    skip_out = np.zeros(1, np.uint8)
 
-    def step(timed, t):
-        pairs = {}
-
-        def bracket(name, fn):
-            if not timed:
-                fn()
-                return
-            a, b = hip.event(), hip.event()
-            hip.record(a, stream)
+    def step(t, ev=None, brackets=False):
+        """One pass of the hot path.  `ev`: name -> (start, stop) events,
+        created beforehand; the GEMM pairs take the dispatch timestamps of
+        the GEMM kernels, the other pairs (only with `brackets`) are
+        recorded around whole library calls."""
+        def call(name, fn):
+            if brackets:
+                hip.record(ev[name][0], stream)
             fn()
-            hip.record(b, stream)
-            pairs[name] = (a, b)
+            if brackets:
+                hip.record(ev[name][1], stream)
 
         def gemm(name, fn):
-            if timed:
-                a, b = hip.event(), hip.event()
-                qa.set_gemm_events(a.value, b.value)
-                pairs[name] = (a, b)
+            if ev is not None:
+                qa.set_gemm_events(ev[name][0].value, ev[name][1].value)
             fn()
-            if timed:
+            if ev is not None:
                 qa.set_gemm_events(None, None)
 
-        bracket("act_quant_nvfp4", lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws))
-        bracket("qlinear_nvfp4", lambda: gemm("gemm_nvfp4", lambda: qa.qlinear_nvfp4(
-            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4)))
-        bracket("act_quant_int8", lambda: qa.act_quant(qa.INT8, xd, a8, s8))
-        bracket("qlinear_int8", lambda: gemm("gemm_int8", lambda: qa.qlinear_int8(
-            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8)))
-        bracket("tdc_update", lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws))
-        bracket("tdc_apply", lambda: qa.tdc_apply(xd, dnew, applied, s2, rws))
+        call("act_quant_nvfp4", lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws,
+                                                     stream=stream))
+        call("qlinear_nvfp4", lambda: gemm("gemm_nvfp4", lambda: qa.qlinear_nvfp4(
+            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4, stream=stream)))
+        call("act_quant_int8", lambda: qa.act_quant(qa.INT8, xd, a8, s8, stream=stream))
+        call("qlinear_int8", lambda: gemm("gemm_int8", lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)))
+        call("tdc_update", lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream))
+        call("tdc_apply", lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream))
         host_sums[:4].copy_(s4, non_blocking=True)
         host_sums[4:].copy_(s2, non_blocking=True)
         torch.cuda.current_stream(dev).synchronize()
-        h = host_sums.numpy()
-        g = qa.gamma_from_sums(h[4:6])
-        d = qa.rel_l2_from_sums(h[:4])
-        qa.dmpq_mask(np.array([g]), alpha, beta, 0.1, 1, 4)
-        qa.tdc_decide(t, [d], [1], 0.05)
-        return pairs
+        gamma_buf[0] = qa.gamma_from_sums(host_np[4:6])
+        d_buf[0] = qa.rel_l2_from_sums(host_np[:4])
+        qa.dmpq_mask(gamma_buf, alpha, beta, 0.1, 1, 4, out=mask_out)
+        qa.tdc_decide(t, d_buf, computed, 0.05, out=skip_out)
+
+    def make_events(keys):
+        return [{k: (hip.event(), hip.event()) for k in keys} for _ in range(args.steps)]
 
     if args.calib_copy:
         # a 256 MiB device copy whose source was written and then evicted
@@ -218,19 +224,33 @@ def main():
         torch.cuda.synchronize()
         del src, dst, flush
     for t in range(args.warmup):
-        step(False, t)
+        step(t)
+    # timed steps: only the two GEMM dispatches carry (in-packet) events
+    timed_ev = make_events(["gemm_nvfp4", "gemm_int8"])
     torch.cuda.synchronize()
-    all_pairs = []
     t0 = time.perf_counter()
     for t in range(args.steps):
-        all_pairs.append(step(True, t))
+        step(t, timed_ev[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for pairs in all_pairs:
-        for k, (a, b) in pairs.items():
-            ev[k].append(hip.ms(a, b))
-            hip.destroy(a)
-            hip.destroy(b)
+    # per-call breakdown of the other kernels: as many extra steps, with
+    # event markers around every library call (outside the timed region)
+    split_ev = make_events(names)
+    for t in range(args.steps):
+        step(t, split_ev[t], brackets=True)
+    torch.cuda.synchronize()
+    ev = {k: [] for k in names}
+    for evs, keys in ((timed_ev, ("gemm_nvfp4", "gemm_int8")),
+                      (split_ev, [k for k in names if not k.startswith("gemm_")])):
+        for pairs in evs:
+            for k in keys:
+                a, b = pairs[k]
+                ev[k].append(hip.ms(a, b))
+    for evs in (timed_ev, split_ev):
+        for pairs in evs:
+            for a, b in pairs.values():
+                hip.destroy(a)
+                hip.destroy(b)
     avg = {k: float(np.mean(v)) for k, v in ev.items() if v}
 
     ms_step = wall * 1e3 / args.steps

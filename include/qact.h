@@ -185,9 +185,10 @@ int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha,
 int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
                double delta, uint8_t* skip);
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
- * inside qlinear) records `before` on its stream just before its main GEMM
- * kernel and `after` just after it, so that the caller can time that kernel
- * alone with hipEventElapsedTime.  The events are created and owned by the
+ * inside qlinear) launches its main GEMM kernel with hipExtLaunchKernel so
+ * that `before` and `after` take that dispatch's start and end timestamps
+ * (no extra packets on the stream); hipEventElapsedTime(before, after) is
+ * then that kernel's duration.  The events are created and owned by the
  * caller; pass NULL, NULL to stop.  Process-wide setting, not thread-safe. */
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after);
 

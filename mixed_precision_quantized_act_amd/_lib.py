@@ -77,14 +77,15 @@ def _check(fn, status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes converts a plain int for a c_void_p parameter
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
     if stream is not None:
-        return ctypes.c_void_p(stream)
+        return stream
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _nbytes(t):
@@ -178,26 +179,44 @@ def tdc_apply(x_in, delta, x_out, sums2=None, ws=None, n=None, stream=None):
 
 # ------------------------------------------------------- host decisions --
 
-def dmpq_mask(gamma_prev, alpha, beta, tau, L, J):
-    """gamma_prev: float64 numpy [L] or None; alpha/beta float32 [L*J]."""
+def _host_array(a, dtype):
+    """`a` as a C-contiguous numpy array of `dtype` (no copy when it already is)."""
     import numpy as np
-    mask = np.zeros(L * J, dtype=np.uint8)
-    a = np.ascontiguousarray(alpha, dtype=np.float32)
-    b = np.ascontiguousarray(beta, dtype=np.float32)
-    g = None if gamma_prev is None else np.ascontiguousarray(gamma_prev, dtype=np.float64)
-    _check("dmpq_mask", lib().dmpq_mask(None if g is None else g.ctypes.data_as(_P), L, J,
-                                        a.ctypes.data_as(_P), b.ctypes.data_as(_P), float(tau),
-                                        mask.ctypes.data_as(_P)))
+    if isinstance(a, np.ndarray) and a.dtype == dtype and a.flags.c_contiguous:
+        return a
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def dmpq_mask(gamma_prev, alpha, beta, tau, L, J, out=None):
+    """gamma_prev: float64 [L] or None; alpha/beta float32 [L*J]; returns the
+    uint8 mask [L*J] (written into `out` when given)."""
+    import numpy as np
+    mask = np.zeros(L * J, dtype=np.uint8) if out is None else out
+    if mask.dtype != np.uint8 or mask.size < L * J or not mask.flags.c_contiguous:
+        raise ValueError("dmpq_mask: out must be a contiguous uint8 array of L*J entries")
+    a = _host_array(alpha, np.float32)
+    b = _host_array(beta, np.float32)
+    if a.size < L * J or b.size < L * J:
+        raise ValueError("dmpq_mask: alpha and beta need L*J entries")
+    g = None if gamma_prev is None else _host_array(gamma_prev, np.float64)
+    if g is not None and g.size < L:
+        raise ValueError("dmpq_mask: gamma_prev needs L entries")
+    _check("dmpq_mask", lib().dmpq_mask(None if g is None else g.ctypes.data, L, J,
+                                        a.ctypes.data, b.ctypes.data, float(tau), mask.ctypes.data))
     return mask
 
 
-def tdc_decide(t, d_prev, computed_prev, delta):
+def tdc_decide(t, d_prev, computed_prev, delta, out=None):
     import numpy as np
-    d = np.ascontiguousarray(d_prev, dtype=np.float64)
-    c = np.ascontiguousarray(computed_prev, dtype=np.uint8)
-    skip = np.zeros(len(d), dtype=np.uint8)
-    _check("tdc_decide", lib().tdc_decide(int(t), d.ctypes.data_as(_P), c.ctypes.data_as(_P),
-                                          len(d), float(delta), skip.ctypes.data_as(_P)))
+    d = _host_array(d_prev, np.float64)
+    c = _host_array(computed_prev, np.uint8)
+    if c.size < d.size:
+        raise ValueError("tdc_decide: computed_prev needs one entry per block")
+    skip = np.zeros(d.size, dtype=np.uint8) if out is None else out
+    if skip.dtype != np.uint8 or skip.size < d.size or not skip.flags.c_contiguous:
+        raise ValueError("tdc_decide: out must be a contiguous uint8 array, one entry per block")
+    _check("tdc_decide", lib().tdc_decide(int(t), d.ctypes.data, c.ctypes.data, d.size, float(delta),
+                                          skip.ctypes.data))
     return skip
 
 
@@ -209,11 +228,15 @@ def set_gemm_events(before, after):
 
 def gamma_from_sums(sums2):
     import numpy as np
-    s = np.ascontiguousarray(sums2, dtype=np.float64)
-    return lib().qa_gamma_from_sums(s.ctypes.data_as(_P))
+    s = _host_array(sums2, np.float64)
+    if s.size < 2:
+        raise ValueError("gamma_from_sums: needs the two sums")
+    return lib().qa_gamma_from_sums(s.ctypes.data)
 
 
 def rel_l2_from_sums(sums4):
     import numpy as np
-    s = np.ascontiguousarray(sums4, dtype=np.float64)
-    return lib().qa_rel_l2_from_sums(s.ctypes.data_as(_P))
+    s = _host_array(sums4, np.float64)
+    if s.size < 4:
+        raise ValueError("rel_l2_from_sums: needs the four sums")
+    return lib().qa_rel_l2_from_sums(s.ctypes.data)
