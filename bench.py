@@ -157,8 +157,8 @@ def main():
     ws8 = qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K), dev)
     dnew = torch.empty(n, dtype=torch.int16, device=dev)
     applied = torch.empty(n, dtype=torch.int16, device=dev)
-    s4 = torch.zeros(4, dtype=torch.float64, device=dev)
-    s2 = torch.zeros(2, dtype=torch.float64, device=dev)
+    sums = torch.zeros(6, dtype=torch.float64, device=dev)   # tdc_update's 4, tdc_apply's 2
+    s4, s2 = sums[:4], sums[4:]
     rws = qa.workspace(qa.reduce_workspace(n), dev)
     host_sums = torch.zeros(6, dtype=torch.float64).pin_memory()
     alpha = np.ones(4, np.float32)
@@ -202,8 +202,7 @@ def main():
             a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)))
         call("tdc_update", lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream))
         call("tdc_apply", lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream))
-        host_sums[:4].copy_(s4, non_blocking=True)
-        host_sums[4:].copy_(s2, non_blocking=True)
+        host_sums.copy_(sums, non_blocking=True)
         torch.cuda.current_stream(dev).synchronize()
         gamma_buf[0] = qa.gamma_from_sums(host_np[4:6])
         d_buf[0] = qa.rel_l2_from_sums(host_np[:4])

@@ -110,7 +110,9 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  * 1e-3.
  * Workspace: qlinear_workspace() bytes (a per-tile copy of the E4M3 scales
  * of the operands, about (M + N) K / 16 bytes), device memory that the
- * call may overwrite.
+ * call may overwrite.  When K is a multiple of 64 and w_s is 4-byte
+ * aligned the INT8 call reads the weight scales in place and uses no
+ * workspace (it may then be NULL).
  * y must not overlap any input.  Requires 0 < K, K % 16 == 0, M, N >= 0.
  * ------------------------------------------------------------------------ */
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);

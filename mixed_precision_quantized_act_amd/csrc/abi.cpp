@@ -122,7 +122,7 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
   {
-    const size_t need = nvfp4_gemm_ws_bytes(M, N, K);
+    const size_t need = nvfp4_gemm_ws_need(M, N, K, w_s);
     if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
   }
   if (!aligned16(ws)) return QA_EALIGN;
@@ -143,7 +143,7 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
   {
-    const size_t need = int8_gemm_ws_bytes(M, N, K);
+    const size_t need = int8_gemm_ws_need(M, N, K, w_s);
     if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
   }
   if (!aligned16(ws)) return QA_EALIGN;

@@ -89,11 +89,18 @@ static inline int64_t units_of(int64_t K) { return (K + kUnitK - 1) / kUnitK; }
 // scale bytes of each row as one word: dst[(tile * units + u) * 256 + r].
 // Rows past `rows` and groups past K/16 read as 0 (a zero scale makes the
 // corresponding fp16 values zero, whatever codes the raw unit holds there).
-// One workgroup per (tile, unit), one thread per row.
+// One workgroup per (tile, unit), one thread per row; the workgroups past
+// tiles0 * units re-lay the second array (s1, rows1, dst1).
 __global__ void __launch_bounds__(256)
-scale_tiles_kernel(const uint8_t* __restrict__ s, int64_t rows, int64_t K, int units,
-                   uint32_t* __restrict__ dst) {
-  const int tu = (int)blockIdx.x;
+scale_tiles_kernel(const uint8_t* __restrict__ s0, int64_t rows0, uint32_t* __restrict__ dst0,
+                   int tiles0, const uint8_t* __restrict__ s1, int64_t rows1,
+                   uint32_t* __restrict__ dst1, int64_t K, int units) {
+  int tu = (int)blockIdx.x;
+  const bool second = tu >= tiles0 * units;
+  if (second) tu -= tiles0 * units;
+  const uint8_t* const s = second ? s1 : s0;
+  const int64_t rows = second ? rows1 : rows0;
+  uint32_t* const dst = second ? dst1 : dst0;
   const int u = tu % units, t = tu / units;
   const int64_t row = (int64_t)t * 256 + threadIdx.x;
   const int64_t gpr = K / 16;
@@ -110,8 +117,6 @@ scale_tiles_kernel(const uint8_t* __restrict__ s, int64_t rows, int64_t K, int u
   }
   dst[(int64_t)tu * 256 + threadIdx.x] = v;
 }
-
-// ------------------------------------------------------------ epilogue --
 
 // GELU, tanh form: 0.5 v (1 + tanh u) = v / (1 + exp(-2u)) with
 // u = sqrt(2/pi) (v + 0.044715 v^3); exp and the reciprocal are the
@@ -139,13 +144,14 @@ struct GemmArgs {
   const uint8_t* a;      // NVFP4 codes [M][K/2] or int8 [M][K]
   const uint32_t* a_st;  // NVFP4: per-tile scale words of A
   const uint8_t* b;      // NVFP4 codes [N][K/2]
-  const uint32_t* b_st;  // per-tile scale words of W
+  const uint32_t* b_st;  // per-tile scale words of W (or the E4M3 array, b_direct)
   int64_t K;
   int units, nk;         // raw units of 64 and fp16 stages of 32 along K
   int mt, nt;            // tile counts
   const float* a_ts;     // NVFP4: activation tensor scale
   const float* w_ts;     // weight tensor scale
   const float* a_rs;     // INT8: per-row activation scale
+  int b_direct;          // W's scale words read from the [N][K/16] array itself
 };
 
 // Raw buffer (stride 0) over [base, base + bytes): loads at offsets >=
@@ -257,10 +263,19 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   const int64_t a_rows = min<int64_t>(e.M - m0, kTileM), b_rows = min<int64_t>(e.N - n0, kTileN);
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.a + m0 * a_row, (uint32_t)(a_rows * a_row));
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(g.b + n0 * b_row, (uint32_t)(b_rows * b_row));
+  // Scale words: word u * 256 + r of the tile's re-laid-out copy holds the
+  // 4 scales of row r and unit u; with b_direct (K a multiple of 64, rows
+  // are whole words) W's word is bytes 4u .. 4u+3 of row r of its array.
+  const uint32_t gpr = (uint32_t)(K / 16);
+  const bool bd = g.b_direct != 0;
   const uint32_t st_bytes = (uint32_t)g.units * 1024u;
+  const uint8_t* const bs_base =
+      bd ? reinterpret_cast<const uint8_t*>(g.b_st) + n0 * gpr
+         : reinterpret_cast<const uint8_t*>(g.b_st + (size_t)tn * g.units * 256);
   const __amdgpu_buffer_rsrc_t ras =
-      buffer_rsrc(I8 ? g.b_st : g.a_st + (size_t)tm * g.units * 256, I8 ? 0u : st_bytes);
-  const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(g.b_st + (size_t)tn * g.units * 256, st_bytes);
+      buffer_rsrc(I8 ? static_cast<const void*>(g.b_st) : g.a_st + (size_t)tm * g.units * 256,
+                  I8 ? 0u : st_bytes);
+  const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(bs_base, bd ? (uint32_t)(b_rows * gpr) : st_bytes);
   constexpr uint32_t kOOB = 0x7FFFFFF0u;
 
   // ---- DMA of raw unit u into slot u % 4.  The destination of one
@@ -296,9 +311,11 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
         dma16(ra, s + R::kA + blk * 1024, real && kb < (uint32_t)K ? row * (uint32_t)a_row + kb : kOOB);
       }
     }
-    const uint32_t so = real ? (uint32_t)u * 1024u + (uint32_t)(64 * wave + lane) * 4u : kOOB;
-    if constexpr (!I8) dma4(ras, s + R::kAS + 256 * wave, so);
-    dma4(rbs, s + R::kBS + 256 * wave, so);
+    const uint32_t srow = (uint32_t)(64 * wave + lane);
+    const uint32_t so_a = (uint32_t)u * 1024u + srow * 4u;
+    const uint32_t so_b = bd ? srow * gpr + 4u * (uint32_t)u : (uint32_t)u * 1024u + srow * 4u;
+    if constexpr (!I8) dma4(ras, s + R::kAS + 256 * wave, real ? so_a : kOOB);
+    dma4(rbs, s + R::kBS + 256 * wave, real ? so_b : kOOB);
   };
   // ---- raw words of a stage.  Lane (h, r) = (lane / 32, lane % 32) of
   // tile i takes row 32 i + r of the wave's rows: for NVFP4 the 8 code
@@ -419,6 +436,16 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     }
   };
 
+  // epilogue scales, read now so that their latency hides under the loop:
+  // the tensor scales and (INT8, plain epilogue) the row scales of the
+  // lane's rows (rows past M read row M-1; they are never stored)
+  const float alpha = I8 ? *g.w_ts : (*g.a_ts) * (*g.w_ts);
+  float row_scale[kFM];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+    row_scale[i] = I8 && kPlain ? g.a_rs[min<int64_t>(m0 + wm * 128 + 32 * i + (lane & 31), e.M - 1)]
+                                : 1.0f;
+
   // ---- pipeline.  Units are issued in order, one per two stages, with
   // units past the last one issued as zero loads, so that a wave always has
   // the same number of DMA instructions in flight and every stage past K
@@ -479,15 +506,13 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   __syncthreads();       // every wave is past its last read of the ring
   const int64_t wave_row0 = m0 + wm * 128;
   const int64_t wave_col0 = n0 + wn * 128;
-  const float alpha = I8 ? *g.w_ts : (*g.a_ts) * (*g.w_ts);
   const int c = lane & 31;
   float rs[kFM];
 #pragma unroll
   for (int i = 0; i < kFM; ++i) {
-    if constexpr (I8)
-      rs[i] = g.a_rs[min<int64_t>(wave_row0 + 32 * i + c, e.M - 1)] * alpha;
-    else
-      rs[i] = alpha;
+    if constexpr (I8 && !kPlain)       // (the general kernel reads them here)
+      row_scale[i] = g.a_rs[min<int64_t>(wave_row0 + 32 * i + c, e.M - 1)];
+    rs[i] = I8 ? row_scale[i] * alpha : alpha;
   }
   if constexpr (kPlain) {
     // bf16 staged per 32-row slice through this wave's own 8 KB of the idle
@@ -505,26 +530,36 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
               u32x2{bf16_pack(a[4 * q] * rs[i], a[4 * q + 1] * rs[i]),
                     bf16_pack(a[4 * q + 2] * rs[i], a[4 * q + 3] * rs[i])};
         }
-      wait_lds();
+      // a wave's LDS operations run in order, so the reads below see these
+      // writes without a wait; the fence only keeps the compiler's order
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      asm volatile("" ::: "memory");
       // this pass's 32 x 128 block: rows below e.M - prow0, columns below
       // e.N - wave_col0 exist
       const int64_t prow0 = wave_row0 + i * 32;
       uint16_t* const ybase = static_cast<uint16_t*>(e.y) + prow0 * e.ldy + wave_col0;
       const int64_t rows_left = e.M - prow0, cols_left = e.N - wave_col0;
+      const int k = lane & 15;
+      u32x4 d[8];
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int r = it * 4 + (lane >> 4), k = lane & 15;
-        const u32x4 d = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((k ^ (r & 15)) << 4));
+        const int r = it * 4 + (lane >> 4);
+        d[it] = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((k ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4);
         if (r < rows_left && k * 8 < cols_left) {
           uint16_t* yp = ybase + (int64_t)r * e.ldy + k * 8;
           if (k * 8 + 8 <= cols_left)
-            *reinterpret_cast<u32x4*>(yp) = d;
+            *reinterpret_cast<u32x4*>(yp) = d[it];
           else
             for (int t = 0; k * 8 + t < cols_left; ++t)
-              yp[t] = (uint16_t)(d[t >> 1] >> (16 * (t & 1)));
+              yp[t] = (uint16_t)(d[it][t >> 1] >> (16 * (t & 1)));
         }
       }
-      wait_lds();
+      // the next pass overwrites the slice after these reads (in order)
+      asm volatile("" ::: "memory");
     }
   } else {
     // general: from registers, 4 consecutive outputs per lane and (i, j, q)
@@ -600,6 +635,23 @@ size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t int8_gemm_ws_bytes(int64_t, int64_t N, int64_t K) { return scale_tiles_bytes(N, K); }
 
+// INT8: the weight scales are read in place when K is a multiple of 64 and
+// the array is 4-byte aligned (no re-layout launch).  The NVFP4 kernel,
+// whose raw loads already touch more rows per unit, measured about 5 %
+// slower reading either scale array in place than after one re-layout
+// launch of both, so it always takes the per-tile copies.
+static bool w_scales_direct(int64_t K, const void* w_s) {
+  return K % kUnitK == 0 && (reinterpret_cast<uintptr_t>(w_s) & 3) == 0;
+}
+
+size_t nvfp4_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void*) {
+  return nvfp4_gemm_ws_bytes(M, N, K);
+}
+
+size_t int8_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void* w_s) {
+  return w_scales_direct(K, w_s) ? 0 : int8_gemm_ws_bytes(M, N, K);
+}
+
 static hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 void set_gemm_events(hipEvent_t before, hipEvent_t after) {
@@ -607,11 +659,14 @@ void set_gemm_events(hipEvent_t before, hipEvent_t after) {
   g_ev_after = after;
 }
 
-static hipError_t launch_scale_tiles(const uint8_t* s, int64_t rows, int64_t K, uint32_t* dst,
+// one launch re-lays out (s0, rows0) and, when s1 is not null, (s1, rows1)
+static hipError_t launch_scale_tiles(const uint8_t* s0, int64_t rows0, uint32_t* dst0,
+                                     const uint8_t* s1, int64_t rows1, uint32_t* dst1, int64_t K,
                                      hipStream_t st) {
-  const int64_t tiles = (rows + kTileM - 1) / kTileM, units = units_of(K);
-  hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)(tiles * units)), dim3(256), 0, st, s, rows,
-                     K, (int)units, dst);
+  const int64_t units = units_of(K);
+  const int64_t t0 = (rows0 + kTileM - 1) / kTileM, t1 = s1 ? (rows1 + kTileM - 1) / kTileM : 0;
+  hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)((t0 + t1) * units)), dim3(256), 0, st, s0,
+                     rows0, dst0, (int)t0, s1, rows1, dst1, K, (int)units);
   return hipGetLastError();
 }
 
@@ -659,17 +714,17 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
                              int64_t M, int64_t N, int64_t K, const GemmOut& o, void* ws,
                              hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  GemmArgs g = base_args(M, N, K);
   uint32_t* a_st = static_cast<uint32_t*>(ws);
   uint32_t* b_st = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
                                                round_up((int64_t)scale_tiles_bytes(M, K), 256));
-  hipError_t err = launch_scale_tiles(a_s, M, K, a_st, st);
-  if (err == hipSuccess) err = launch_scale_tiles(w_s, N, K, b_st, st);
+  hipError_t err = launch_scale_tiles(a_s, M, a_st, w_s, N, b_st, K, st);
   if (err != hipSuccess) return err;
-  GemmArgs g = base_args(M, N, K);
-  g.a = a_q;
+  g.b_direct = 0;
   g.a_st = a_st;
-  g.b = w_q;
   g.b_st = b_st;
+  g.a = a_q;
+  g.b = w_q;
   g.a_ts = a_ts;
   g.w_ts = w_ts;
   EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
@@ -680,13 +735,18 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
                             const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
                             int64_t K, const GemmOut& o, void* ws, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  uint32_t* b_st = static_cast<uint32_t*>(ws);
-  hipError_t err = launch_scale_tiles(w_s, N, K, b_st, st);
-  if (err != hipSuccess) return err;
   GemmArgs g = base_args(M, N, K);
+  g.b_direct = w_scales_direct(K, w_s);
+  if (g.b_direct) {
+    g.b_st = reinterpret_cast<const uint32_t*>(w_s);
+  } else {
+    uint32_t* b_st = static_cast<uint32_t*>(ws);
+    hipError_t err = launch_scale_tiles(w_s, N, b_st, nullptr, 0, nullptr, K, st);
+    if (err != hipSuccess) return err;
+    g.b_st = b_st;
+  }
   g.a = reinterpret_cast<const uint8_t*>(a_q);
   g.b = w_q;
-  g.b_st = b_st;
   g.w_ts = w_ts;
   g.a_rs = a_s;
   EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};

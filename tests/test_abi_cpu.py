@@ -68,6 +68,13 @@ def test_qlinear_validation():
     assert _status("qlinear_nvfp4", None, *ok[1:], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, big, None) == -1
     assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
     assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900001), 4, 0, 0, FAKE, big, None) == -3
+    # INT8 with K a multiple of 64 reads the weight scales in place, only
+    # from a 4-byte aligned array; otherwise the workspace is needed (NVFP4
+    # always needs it)
+    odd = ctypes.c_void_p(FAKE.value + 1)
+    assert _status("qlinear_nvfp4", *ok, 4, 4, 64, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:3], odd, FAKE, 4, 4, 64, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:5], 4, 4, 80, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
     # per-tile copies of the E4M3 scales: 4 bytes per row and K unit of 64,
     # rows rounded up to tiles of 256
     units = (1920 + 63) // 64

@@ -270,3 +270,39 @@ def test_strided_output_bias_gelu(path, out_f32):
         assert rel_fro(got, _round_ref(ref, out_f32)) <= TOL
         rest = t.cat([big[:, :off], big[:, off + N:]], dim=1).float().cpu().numpy()
         assert np.all(rest == -7.0)
+
+
+def _dev_at_odd_offset(a):
+    """Device copy of `a` whose first byte sits at an odd address."""
+    raw = np.concatenate([np.zeros(1, np.uint8), np.ascontiguousarray(a).view(np.uint8).ravel()])
+    return dev(raw)[1:]
+
+
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+@pytest.mark.parametrize("where", ["in_place", "odd_address"])
+def test_scale_sources(path, where):
+    # K a multiple of 64: the INT8 call reads an aligned weight-scale array
+    # in place (it gets no workspace at all); scale arrays at odd addresses
+    # go through the per-tile copies in the workspace.  Both must give the
+    # oracle's product.
+    qa, t = _qa(), torch()
+    M, N, K = 300, 200, 192
+    x, w = _case(M, N, K, seed=23)
+    wq = Q.nvfp4_encode(w)
+    put = _dev_at_odd_offset if where == "odd_address" else dev
+    y = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    if path == "nvfp4":
+        a = Q.nvfp4_encode(x)
+        ref = G.linear_ref(Q.nvfp4_decode(*a), Q.nvfp4_decode(*wq))
+        ws = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, N, K))
+        qa.qlinear_nvfp4(dev(a[0]), put(a[1]), dev(np.array([a[2]], np.float32)),
+                         dev(wq[0]), put(wq[1]), dev(np.array([wq[2]], np.float32)), y, M, N, K,
+                         ws=ws)
+    else:
+        a = Q.int8_encode(x)
+        ref = G.linear_ref(Q.int8_decode(*a), Q.nvfp4_decode(*wq))
+        ws = None if where == "in_place" else qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K))
+        qa.qlinear_int8(dev(a[0]), dev(a[1]), dev(wq[0]), put(wq[1]),
+                        dev(np.array([wq[2]], np.float32)), y, M, N, K, ws=ws)
+    t.cuda.synchronize()
+    assert rel_fro(_out_host(y, False), _round_ref(ref, False)) <= TOL
