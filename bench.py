@@ -16,7 +16,11 @@ steps (2 * 2*M*N*K per step).  The GEMM kernel times come from HIP events
 that the library's hook attaches to the GEMM dispatches themselves inside
 the timed steps (their start and end timestamps, on the launch stream);
 the times of the other calls come from event markers around each library
-call in as many extra, untimed steps after the timed region.
+call in as many extra, untimed steps after the timed region.  `cold`
+times each bandwidth-bound call alone, after a 1 GiB read that evicts L2
+and the Infinity Cache (median of --cold-reps), against the algorithmic
+bytes of the call (the NVFP4 amax pre-pass is not counted; the
+given-tensor-scale call is the encoder alone).
 """
 import argparse
 import ctypes
@@ -114,6 +118,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cold-reps", type=int, default=9,
+                    help="reps of each bandwidth kernel timed after a 1 GiB cache-evicting read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (counter calibration)")
@@ -252,6 +258,42 @@ def main():
                 hip.destroy(b)
     avg = {k: float(np.mean(v)) for k, v in ev.items() if v}
 
+    # the bandwidth kernels timed cold: before each rep a 1 GiB device read
+    # replaces the contents of L2 and the 256 MB Infinity Cache with clean
+    # lines (after a write, the write-back of its dirty lines would land in
+    # the timed kernel); median of the reps
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    gw = qa.workspace(qa.reduce_workspace(n), dev)
+    gsums = torch.zeros(2, dtype=torch.float64, device=dev)
+    cold_calls = [
+        ("act_quant_nvfp4", 2.5625 * n, lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws,
+                                                             stream=stream)),
+        ("act_quant_nvfp4_given_tscale", 2.5625 * n,
+         lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, qa.TSCALE_GIVEN, None, stream=stream)),
+        ("act_quant_int8", 3.0 * n + 4 * M, lambda: qa.act_quant(qa.INT8, xd, a8, s8, stream=stream)),
+        ("block_gamma", 4.0 * n, lambda: qa.block_gamma(xd, xod, gsums, gw, stream=stream)),
+        ("tdc_update", 8.0 * n, lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream)),
+        ("tdc_apply", 6.0 * n, lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream)),
+    ]
+    cold = {}
+    for name, nbytes, fn in cold_calls:
+        reps = []
+        for r in range(args.cold_reps):
+            scratch.sum()
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            reps.append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        t = float(np.median(reps))
+        cold[name] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4),
+                      "algorithmic_bytes": int(nbytes)}
+    del scratch
+
     ms_step = wall * 1e3 / args.steps
     flops_step = 2 * 2.0 * M * N * K
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -305,6 +347,7 @@ def main():
                    "activations": "N(0,1) bf16, 19 outlier channels x30",
                    "weights": "N(0,0.02^2) -> NVFP4", "parallelism": "none (1 GPU)"},
         "kernels": kern,
+        "cold": cold,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

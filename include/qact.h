@@ -166,6 +166,17 @@ int tdc_update(const uint16_t* in, const uint16_t* out, const uint16_t* delta_pr
 int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
               double* sums2, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* rel_err (Fig. 3 caption: E_rel, the layer-wise relative quantization
+ * error at a timestep, to which the DMPQ predictor is fitted; read here as
+ * the relative L2 error of the layer output against its bf16 computation):
+ *   sums2 = { sum (y_q - y_ref)^2, sum y_ref^2 } over bf16 [n] arrays
+ *   (device, 16-byte aligned), float64 device output; E_rel =
+ *   sqrt(sums2[0]) / sqrt(sums2[1]) (qa_rel_err_from_sums; 0/0 = 0,
+ *   x/0 = +inf).  Workspace: reduce_workspace(n) bytes, as for the Gamma
+ *   and TDC sums; sums2 must not lie in it. */
+int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2,
+            void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Host-side decisions (pure functions on HOST arrays; no GPU work).
  *
@@ -184,6 +195,18 @@ int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t 
  * ------------------------------------------------------------------------ */
 int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha,
               const float* beta, double tau, uint8_t* mask);
+/* dmpq_fit (Fig. 3 caption: over a calibration run, the time-shifted pairs
+ * of a block's Gamma at t-1 and each internal linear's E_rel at t give a
+ * linear regression y = alpha x + beta per linear):  gamma [T][L] (block l
+ * at timestep t), erel [T][L*J] (linear l*J+j at timestep t), host arrays.
+ * For every linear the pairs (gamma[t-1][l], erel[t][l*J+j]), t = 1..T-1,
+ * with both values finite, are fitted by ordinary least squares (centred
+ * sums in long double); alpha/beta [L*J] float32 host outputs, rounded to
+ * nearest.  Fewer than two distinct x: alpha = 0 and beta = the mean of y
+ * (0 without pairs).  Errors: QA_EINVAL for negative sizes, J <= 0 or null
+ * arrays that are needed. */
+int dmpq_fit(const double* gamma, const double* erel, int T, int L, int J, float* alpha,
+             float* beta);
 int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
                double delta, uint8_t* skip);
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
@@ -197,6 +220,7 @@ int qa_set_gemm_events(hipEvent_t before, hipEvent_t after);
 /* Helpers for the host: Gamma and d from the device sums once copied back. */
 double qa_gamma_from_sums(const double* sums2);
 double qa_rel_l2_from_sums(const double* sums4);
+double qa_rel_err_from_sums(const double* sums2);
 
 #ifdef __cplusplus
 }

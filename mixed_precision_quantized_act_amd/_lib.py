@@ -46,11 +46,14 @@ _SIGS = {
     "block_gamma": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_update": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_apply": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "rel_err": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "dmpq_fit": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]),
     "dmpq_mask": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_double, _P]),
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
     "qa_set_gemm_events": (ctypes.c_int, [_P, _P]),
     "qa_gamma_from_sums": (ctypes.c_double, [_P]),
     "qa_rel_l2_from_sums": (ctypes.c_double, [_P]),
+    "qa_rel_err_from_sums": (ctypes.c_double, [_P]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -177,6 +180,13 @@ def tdc_apply(x_in, delta, x_out, sums2=None, ws=None, n=None, stream=None):
                                         _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
+def rel_err(y_q, y_ref, sums2, ws, n=None, stream=None):
+    """sums2 <- {sum (y_q - y_ref)^2, sum y_ref^2} over bf16 device arrays."""
+    n = y_q.numel() if n is None else n
+    _check("rel_err", lib().rel_err(_ptr(y_q), _ptr(y_ref), n, _ptr(sums2), _ptr(ws),
+                                    _nbytes(ws), _stream(stream)))
+
+
 # ------------------------------------------------------- host decisions --
 
 def _host_array(a, dtype):
@@ -220,6 +230,22 @@ def tdc_decide(t, d_prev, computed_prev, delta, out=None):
     return skip
 
 
+def dmpq_fit(gamma, erel, J):
+    """Per-linear (alpha, beta) float32 [L*J] from gamma [T, L] and erel
+    [T, L*J] (host arrays; pairs gamma[t-1], erel[t])."""
+    import numpy as np
+    g = _host_array(gamma, np.float64)
+    e = _host_array(erel, np.float64)
+    if g.ndim != 2 or e.ndim != 2 or e.shape != (g.shape[0], g.shape[1] * J):
+        raise ValueError("dmpq_fit: gamma must be [T, L] and erel [T, L*J]")
+    T, L = g.shape
+    alpha = np.zeros(L * J, np.float32)
+    beta = np.zeros(L * J, np.float32)
+    _check("dmpq_fit", lib().dmpq_fit(g.ctypes.data, e.ctypes.data, T, L, J, alpha.ctypes.data,
+                                      beta.ctypes.data))
+    return alpha, beta
+
+
 def set_gemm_events(before, after):
     """Record raw hipEvent_t handles (ints) around every main GEMM kernel;
     (None, None) stops."""
@@ -232,6 +258,14 @@ def gamma_from_sums(sums2):
     if s.size < 2:
         raise ValueError("gamma_from_sums: needs the two sums")
     return lib().qa_gamma_from_sums(s.ctypes.data)
+
+
+def rel_err_from_sums(sums2):
+    import numpy as np
+    s = _host_array(sums2, np.float64)
+    if s.size < 2:
+        raise ValueError("rel_err_from_sums: needs the two sums")
+    return lib().qa_rel_err_from_sums(s.ctypes.data)
 
 
 def rel_l2_from_sums(sums4):

@@ -3,6 +3,9 @@
 // caption and the Temporal Delta Cache skip rule of the Fig. 2 caption).
 // Every device entry point validates everything before it enqueues work.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <new>
 #include <math.h>
 #include <stdint.h>
 
@@ -246,6 +249,14 @@ int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t 
   return hip_status(launch_tdc(2, in, delta, nullptr, out, n, sums2, ws, stream));
 }
 
+int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2, void* ws,
+            size_t ws_bytes, hipStream_t stream) {
+  if (!sums2) return QA_EINVAL;
+  if (int s = check_stream(y_q, y_ref, n, ws, ws_bytes, true)) return s;
+  if (overlap(sums2, 16, ws, ws_bytes)) return QA_EALIAS;
+  return hip_status(launch_tdc(3, y_q, y_ref, nullptr, nullptr, n, sums2, ws, stream));
+}
+
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
   set_gemm_events(before, after);
@@ -265,6 +276,62 @@ double qa_gamma_from_sums(const double* sums2) {
 
 double qa_rel_l2_from_sums(const double* sums4) {
   return sums4 ? ratio0(sqrt(sums4[2]), sqrt(sums4[3])) : NAN;
+}
+
+double qa_rel_err_from_sums(const double* sums2) {
+  return sums2 ? ratio0(sqrt(sums2[0]), sqrt(sums2[1])) : NAN;
+}
+
+// Least-squares line y = alpha x + beta through n points (two passes:
+// means, then centred sums, in long double).  Fewer than two distinct x:
+// alpha = 0 and beta = mean of y (0 without points).
+static void fit_line(const long double* x, const long double* y, int n, float* alpha,
+                     float* beta) {
+  if (n == 0) {
+    *alpha = 0.0f;
+    *beta = 0.0f;
+    return;
+  }
+  long double mx = 0, my = 0;
+  for (int i = 0; i < n; ++i) {
+    mx += x[i];
+    my += y[i];
+  }
+  mx /= n;
+  my /= n;
+  long double sxx = 0, sxy = 0;
+  for (int i = 0; i < n; ++i) {
+    sxx += (x[i] - mx) * (x[i] - mx);
+    sxy += (x[i] - mx) * (y[i] - my);
+  }
+  const long double a = sxx > 0 ? sxy / sxx : 0.0L;
+  *alpha = (float)a;
+  *beta = (float)(my - a * mx);
+}
+
+int dmpq_fit(const double* gamma, const double* erel, int T, int L, int J, float* alpha,
+             float* beta) {
+  if (T < 0 || L < 0 || J <= 0 || !alpha || !beta) return QA_EINVAL;
+  if ((T > 0 && L > 0) && (!gamma || !erel)) return QA_EINVAL;
+  const int np = T > 1 ? T - 1 : 0;
+  long double* x = np ? new (std::nothrow) long double[2 * (size_t)np] : nullptr;
+  if (np && !x) return QA_EINVAL;
+  long double* y = x ? x + np : nullptr;
+  for (int l = 0; l < L; ++l)
+    for (int j = 0; j < J; ++j) {
+      int n = 0;
+      for (int t = 1; t < T; ++t) {
+        const double g = gamma[(size_t)(t - 1) * L + l];
+        const double e = erel[(size_t)t * L * J + (size_t)l * J + j];
+        if (!std::isfinite(g) || !std::isfinite(e)) continue;
+        x[n] = g;
+        y[n] = e;
+        ++n;
+      }
+      fit_line(x, y, n, &alpha[(size_t)l * J + j], &beta[(size_t)l * J + j]);
+    }
+  delete[] x;
+  return QA_OK;
 }
 
 int dmpq_mask(const double* gamma_prev, int L, int J, const float* alpha, const float* beta,

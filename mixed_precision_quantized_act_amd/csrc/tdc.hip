@@ -1,9 +1,12 @@
-// Gamma and Temporal Delta Cache kernels for gfx950 (HBM-bound streams).
+// Gamma, Temporal Delta Cache and relative-error kernels for gfx950
+// (HBM-bound streams).
 //
 // 6Bit-Diffusion: Gamma is the relative L1 distance between a block's input
 // and output (Fig. 2 and Fig. 3 captions); TDC caches the block residual
 // Delta = out - in and reuses it for invariant blocks (abstract), comparing
-// successive Deltas by relative L2 (Fig. 4 caption).
+// successive Deltas by relative L2 (Fig. 4 caption); E_rel, the layer-wise
+// relative quantization error that the DMPQ predictor is fitted to (Fig. 3
+// caption), is taken as the relative L2 error of the layer output.
 //
 // tdc_apply may run in place (dst == in): every element is read and then
 // written by the same thread, so `in` and `dst` carry no restrict.
@@ -27,7 +30,7 @@ static constexpr int kRedBlocks = QACT_TDC_BLOCKS;
 static constexpr int kThreads = 256;
 static constexpr int kUnroll = QACT_TDC_UNROLL;
 
-enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2 };
+enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3 };
 
 struct Acc4 {
   double s[4];
@@ -38,6 +41,14 @@ __device__ __forceinline__ uint32_t tdc_pair(uint32_t xi, uint32_t bi, uint32_t 
   // xi, bi, pi: bf16 bit patterns (low 16 bits); returns the bf16 written
   const float x = __uint_as_float(xi << 16);
   const float b = __uint_as_float(bi << 16);
+  if (MODE == MODE_RELERR) {
+    // x = quantized output, b = reference: (x - b)^2 and b^2, each exact in
+    // float64 (a bf16 difference has at most 17 significant bits)
+    const double d = (double)x - (double)b;
+    a.s[0] = __fma_rn(d, d, a.s[0]);
+    a.s[1] = __fma_rn((double)b, (double)b, a.s[1]);
+    return 0;
+  }
   if (MODE == MODE_APPLY) {
     const uint32_t o = f32_to_bf16(x + b);
     const double od = (double)__uint_as_float(o << 16);
@@ -94,7 +105,7 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
         const uint32_t hi = tdc_pair<MODE, PREV>(xv[u][i] >> 16, bv[u][i] >> 16, pv[u][i] >> 16, a);
         ov[i] = lo | (hi << 16);
       }
-      if (MODE != MODE_GAMMA && v < nvec)
+      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && v < nvec)
         __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst) + v);
     }
   }
@@ -103,7 +114,7 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
     const int64_t e = nvec * 8 + threadIdx.x;
     if (e < n) {
       const uint32_t o = tdc_pair<MODE, PREV>(in[e], b[e], PREV ? prev[e] : 0u, a);
-      if (MODE != MODE_GAMMA) dst[e] = (uint16_t)o;
+      if (MODE != MODE_GAMMA && MODE != MODE_RELERR) dst[e] = (uint16_t)o;
     }
   }
   if (!want_sums) return;
@@ -171,8 +182,11 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   else if (mode == MODE_UPDATE)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, false>), g, t, 0, stream, in, b, prev, dst, n,
                        partial, want);
-  else
+  else if (mode == MODE_APPLY)
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY, false>), g, t, 0, stream, in, b, prev, dst, n,
+                       partial, want);
+  else
+    hipLaunchKernelGGL((tdc_kernel<MODE_RELERR, false>), g, t, 0, stream, in, b, prev, dst, n,
                        partial, want);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !want) return e;

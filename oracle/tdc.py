@@ -28,7 +28,16 @@ Readings taken where the pages are silent:
     and measures d against the cached Delta it replaces.
   * Delta and outputs are bfloat16 rounded once (nearest-even) from the
     exact sum/difference; the norms are square roots of float64 sums.
+  * E_rel (the layer-wise relative quantization error of Fig. 3) is the
+    relative L2 error ||Y_q - Y||_2 / ||Y||_2 of a linear's bf16 output
+    against the bf16 output of the unquantized linear (0/0 = 0, x/0 = inf).
+  * The fit of Fig. 3 is ordinary least squares on the time-shifted pairs
+    (Gamma_{t-1} of the block, E_rel_t of the linear), t = 1..T-1, pairs
+    with a non-finite value dropped; alpha and beta are the exact
+    least-squares values rounded to float32 (nearest-even).  Fewer than two
+    distinct x: alpha = 0, beta = mean of y (0 without pairs).
 """
+from fractions import Fraction
 import math
 
 import numpy as np
@@ -142,6 +151,71 @@ def tdc_decide(t, d_prev, computed_prev, delta):
     if t < 2:
         return np.zeros(d_prev.shape, dtype=np.uint8)
     return (computed_prev & (d_prev < float(delta))).astype(np.uint8)
+
+
+def rel_err_sums(yq_bits, yref_bits):
+    """(sum (y_q - y)^2, sum y^2), each correctly rounded (exact terms)."""
+    q = bf16_to_f64(yq_bits).ravel()
+    r = bf16_to_f64(yref_bits).ravel()
+    return _fsum((q - r) ** 2), _fsum(r ** 2)
+
+
+def rel_err(s0, s1):
+    """E_rel = sqrt(s0) / sqrt(s1) from the two sums."""
+    return ratio(math.sqrt(s0), math.sqrt(s1))
+
+
+def fraction_to_f32(q):
+    """A rational rounded to the nearest float32 (ties to even); |q| stays
+    well inside the normal float32 range in every use here."""
+    q = Fraction(q)
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # a in [2^e, 2^(e+1)): 24 significant bits -> unit 2^(e-23)
+    scaled = a / Fraction(2) ** (e - 23)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return np.float32(sign * float(Fraction(m) * Fraction(2) ** (e - 23)))
+
+
+def fit_line(x, y):
+    """Least-squares (alpha, beta) of y = alpha x + beta, in exact rational
+    arithmetic, rounded to float32."""
+    xs = [Fraction(float(v)) for v in np.asarray(x, np.float64).ravel()]
+    ys = [Fraction(float(v)) for v in np.asarray(y, np.float64).ravel()]
+    n = len(xs)
+    if n == 0:
+        return np.float32(0.0), np.float32(0.0)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((a - mx) ** 2 for a in xs)
+    sxy = sum((a - mx) * (b - my) for a, b in zip(xs, ys))
+    alpha = sxy / sxx if sxx else Fraction(0)
+    return fraction_to_f32(alpha), fraction_to_f32(my - alpha * mx)
+
+
+def calibrate(gamma, erel, n_linears):
+    """Per-linear (alpha, beta) from gamma [T, L] and erel [T, L*J]: the
+    pairs (gamma[t-1, l], erel[t, l*J + j]) for t >= 1 with both finite."""
+    g = np.asarray(gamma, np.float64)
+    e = np.asarray(erel, np.float64)
+    T, L = g.shape
+    J = n_linears
+    alpha = np.zeros(L * J, np.float32)
+    beta = np.zeros(L * J, np.float32)
+    for l in range(L):
+        for j in range(J):
+            x = g[:T - 1, l]
+            y = e[1:, l * J + j]
+            ok = np.isfinite(x) & np.isfinite(y)
+            alpha[l * J + j], beta[l * J + j] = fit_line(x[ok], y[ok])
+    return alpha, beta
 
 
 class BlockCache:

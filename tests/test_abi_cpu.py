@@ -128,3 +128,43 @@ def test_sum_helpers():
     assert qa.gamma_from_sums([0.0, 0.0]) == 0.0
     assert qa.gamma_from_sums([1.0, 0.0]) == float("inf")
     assert qa.rel_l2_from_sums([0, 0, 6.25 * 2.0 ** -10, 6.25]) == 0.03125
+
+
+def test_dmpq_fit_matches_oracle():
+    # host function: the long-double least squares equals the oracle's exact
+    # rational fit rounded to float32, pairs (Gamma_{t-1}, E_rel_t)
+    from oracle import tdc as T
+    rng = np.random.default_rng(21)
+    Tn, L, J = 9, 4, 3
+    g = rng.uniform(0.0, 0.3, (Tn, L))
+    e = np.repeat(g, J, axis=1) * 0.7 + 0.02 + 0.005 * rng.standard_normal((Tn, L * J))
+    e = np.roll(e, 1, axis=0)                  # E_rel_t follows Gamma_{t-1}
+    e[0] = np.nan
+    e[4, 5] = np.inf                           # dropped pair
+    g[6, 2] = np.nan                           # drops (Gamma_6, E_rel_7) of block 2
+    a, b = qa.dmpq_fit(g, e, J)
+    ao, bo = T.calibrate(g, e, J)
+    assert np.array_equal(a, ao) and np.array_equal(b, bo), (a - ao, b - bo)
+
+
+def test_dmpq_fit_degenerate_and_validation():
+    g = np.full((5, 1), 0.1)                   # one x value: alpha 0, beta = mean
+    e = np.array([[np.nan], [1.0], [2.0], [3.0], [6.0]])
+    a, b = qa.dmpq_fit(g, e, 1)
+    assert a[0] == 0.0 and b[0] == 3.0
+    a, b = qa.dmpq_fit(np.zeros((1, 2)), np.zeros((1, 2)), 1)   # T = 1: no pairs
+    assert np.all(a == 0) and np.all(b == 0)
+    f = qa.lib().dmpq_fit
+    out = np.zeros(4, np.float32)
+    assert f(None, None, 3, 2, 0, out.ctypes.data, out.ctypes.data) == -1   # J <= 0
+    assert f(None, None, 3, 2, 1, out.ctypes.data, out.ctypes.data) == -1   # arrays needed
+    assert f(None, None, 0, 2, 1, out.ctypes.data, out.ctypes.data) == 0    # T = 0: nothing to read
+    assert qa.rel_err_from_sums(np.array([1.0, 25.0])) == 0.2
+    assert qa.rel_err_from_sums(np.array([0.0, 0.0])) == 0.0
+    assert qa.rel_err_from_sums(np.array([1.0, 0.0])) == float("inf")
+
+
+def test_rel_err_validation():
+    assert _status("rel_err", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
+    assert _status("rel_err", FAKE, FAKE, 64, FAKE, None, 0, None) == -5
+    assert _status("rel_err", FAKE, FAKE_ODD, 64, FAKE, FAKE, 1 << 20, None) == -3

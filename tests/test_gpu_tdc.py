@@ -169,3 +169,32 @@ def test_block_cache_teacher_forced():
             last, n_stored, computed_prev = nxt, min(n_stored + 1, 2), True
             pattern.append("C")
     assert "S" in pattern and pattern[:2] == ["C", "C"]
+
+
+def gpu_rel_err(q, r):
+    qa, t = _qa(), torch()
+    sums = t.zeros(2, dtype=t.float64, device="cuda")
+    ws = qa.workspace(qa.reduce_workspace(len(q)))
+    qa.rel_err(dev(q), dev(r), sums, ws)
+    t.cuda.synchronize()
+    return host(sums)
+
+
+@pytest.mark.parametrize("n", [65536, 8, 13, 1, 1000003, 17776 * 1920])
+def test_rel_err(n):
+    r, q = pair(n, seed=31, scale=0.02)
+    got = gpu_rel_err(q, r)
+    want = T.rel_err_sums(q, r) if n <= 1000003 else (
+        T._psum((F.bf16_to_f64(q) - F.bf16_to_f64(r)) ** 2), T._psum(F.bf16_to_f64(r) ** 2))
+    _close(got, want)
+    qa = _qa()
+    e = qa.rel_err_from_sums(got)
+    assert abs(e - T.rel_err(*want)) <= 1e-12 * T.rel_err(*want)
+
+
+def test_rel_err_worked_example():
+    r = F.f64_to_bf16_rne(np.array([3.0, 4.0] + [0.0] * 14))
+    q = F.f64_to_bf16_rne(np.array([3.0, 5.0] + [0.0] * 14))
+    got = gpu_rel_err(q, r)
+    assert list(got) == [1.0, 25.0]
+    assert _qa().rel_err_from_sums(got) == 0.2

@@ -2,6 +2,7 @@
 closed forms, and the skip pattern of the state machine on scripted runs."""
 import copy
 import fractions
+from fractions import Fraction
 import math
 
 import numpy as np
@@ -168,3 +169,93 @@ def test_pairwise_sums_within_bound():
     _, pair = T.tdc_update(x, y, pb, summation="pairwise")
     for a, b in zip(exact, pair):
         assert abs(a - b) <= 21 * 2.0 ** -53 * abs(a)
+
+
+# ---- E_rel and the predictor fit (Fig. 3 caption) ----
+
+def test_rel_err_worked_values():
+    # reference (3, 4) has norm 5; output (3, 5) differs by (0, 1): E_rel = 1/5
+    ref = F.f64_to_bf16_rne(np.array([3.0, 4.0]))
+    out = F.f64_to_bf16_rne(np.array([3.0, 5.0]))
+    s0, s1 = T.rel_err_sums(out, ref)
+    assert (s0, s1) == (1.0, 25.0)
+    assert T.rel_err(s0, s1) == 0.2
+    z = F.f64_to_bf16_rne(np.zeros(2))
+    assert T.rel_err(*T.rel_err_sums(z, z)) == 0.0
+    assert T.rel_err(*T.rel_err_sums(out, z)) == math.inf
+
+
+def test_rel_err_equals_norm_ratio():
+    rng = np.random.default_rng(7)
+    r = F.f64_to_bf16_rne(rng.standard_normal(999))
+    q = F.f64_to_bf16_rne(F.bf16_to_f64(r) + 0.01 * rng.standard_normal(999))
+    qa, ra = F.bf16_to_f64(q), F.bf16_to_f64(r)
+    want = np.linalg.norm(qa - ra) / np.linalg.norm(ra)
+    assert abs(T.rel_err(*T.rel_err_sums(q, r)) - want) <= 1e-14 * want
+
+
+def test_fraction_to_f32_rounding():
+    # exact float32 values stay; halfway cases go to even; matches numpy's
+    # correctly rounded float64 -> float32 where the input is a float64
+    assert T.fraction_to_f32(Fraction(3, 4)) == np.float32(0.75)
+    one_ulp = Fraction(1, 2 ** 23)
+    assert T.fraction_to_f32(1 + one_ulp / 2) == np.float32(1.0)            # tie -> even
+    assert T.fraction_to_f32(1 + 3 * one_ulp / 2) == np.float32(1 + 2 * 2 ** -23)
+    assert T.fraction_to_f32(-(1 + one_ulp / 2 + Fraction(1, 2 ** 60))) == np.float32(-(1 + 2 ** -23))
+    rng = np.random.default_rng(3)
+    for v in rng.standard_normal(200) * 10.0 ** rng.integers(-6, 6, 200):
+        assert T.fraction_to_f32(Fraction(float(v))) == np.float32(v)
+
+
+def test_fit_exact_line():
+    x = np.array([0.0, 0.125, 0.5, 1.0, 3.0])
+    y = 2.5 * x - 0.75                         # exact in binary
+    assert T.fit_line(x, y) == (np.float32(2.5), np.float32(-0.75))
+
+
+def test_fit_matches_polyfit():
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        n = int(rng.integers(3, 40))
+        x = rng.uniform(0, 0.3, n)
+        y = 0.8 * x + 0.02 + 0.01 * rng.standard_normal(n)
+        a, b = T.fit_line(x, y)
+        pa, pb = np.polyfit(x, y, 1)
+        assert abs(float(a) - pa) <= 2e-7 * abs(pa) + 1e-12
+        assert abs(float(b) - pb) <= 2e-7 * abs(pb) + 1e-12
+
+
+def test_fit_invariances_and_degenerate():
+    rng = np.random.default_rng(12)
+    x, y = rng.uniform(0, 1, 9), rng.uniform(0, 1, 9)
+    a, b = T.fit_line(x, y)
+    a2, b2 = T.fit_line(x, 2 * y)              # scaling by 2 is exact
+    assert (a2, b2) == (np.float32(2 * float(a)), np.float32(2 * float(b)))
+    a3, b3 = T.fit_line(x, y + 0.5)            # shift moves only beta
+    assert a3 == a and abs(float(b3) - (float(b) + 0.5)) <= 2 ** -23
+    assert T.fit_line([], []) == (np.float32(0), np.float32(0))
+    assert T.fit_line([0.3], [0.7]) == (np.float32(0), np.float32(0.7))
+    assert T.fit_line([0.3, 0.3, 0.3], [1.0, 2.0, 6.0]) == (np.float32(0), np.float32(3.0))
+
+
+def test_calibrate_time_shift():
+    # E_rel at t is exactly 3 Gamma_{t-1} + 0.25 for every linear; pairing
+    # Gamma_t with E_rel_t instead would not fit a line at all
+    rng = np.random.default_rng(13)
+    Tn, L, J = 7, 3, 2
+    g = rng.uniform(0.01, 0.2, (Tn, L))
+    e = np.full((Tn, L * J), np.nan)
+    for t in range(1, Tn):
+        for l in range(L):
+            for j in range(J):
+                e[t, l * J + j] = (3.0 + j) * g[t - 1, l] + 0.25
+    a, b = T.calibrate(g, e, J)
+    for l in range(L):
+        for j in range(J):
+            assert abs(float(a[l * J + j]) - (3.0 + j)) <= 4e-7 * (3.0 + j)
+            assert abs(float(b[l * J + j]) - 0.25) <= 1e-6
+    # a non-finite value drops its pair only
+    e2 = e.copy()
+    e2[3, 0] = np.inf
+    a2, _ = T.calibrate(g, e2, J)
+    assert abs(float(a2[0]) - 3.0) <= 4e-7 * 3
