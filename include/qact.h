@@ -93,6 +93,31 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * qlinear_nvfp4_q / qlinear_int8_q: the same linears with the output
+ * quantized to NVFP4 in the GEMM epilogue, for a consumer linear that
+ * takes NVFP4 activations (6Bit-Diffusion, Fig. 2 caption: the activations
+ * of each internal linear are quantized; fusing that quantization into the
+ * producer removes the bf16 round trip of the intermediate).  Every output
+ * value (scale, bias, GELU as for qlinear_*) is rounded to bf16 and then
+ * encoded exactly as act_quant NVFP4 with QA_TSCALE_GIVEN and tensor scale
+ * *y_ts (device float32, read by the kernel): y_q u8 [M][N/2] codes (low
+ * nibble first), y_s u8 [M][N/16] E4M3 scales.  The tensor scale is an
+ * input because the whole output's |max| is not known while the output
+ * tiles are produced.  Requires N % 16 == 0; y_q 16-byte aligned; y_q and
+ * y_s must not overlap each other, the inputs or the workspace.
+ * Workspace: as for qlinear_nvfp4 / qlinear_int8.
+ * ------------------------------------------------------------------------ */
+int qlinear_nvfp4_q(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                    const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                    int64_t M, int64_t N, int64_t K, const uint16_t* bias, qa_epi epi,
+                    const float* y_ts, uint8_t* y_q, uint8_t* y_s, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                   const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
+                   const uint16_t* bias, qa_epi epi, const float* y_ts, uint8_t* y_q,
+                   uint8_t* y_s, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Quantized linear  Y[M][N] = dequant(A) dequant(W)^T (+ bias) (-> GELU).
  * Abstract and Fig. 2: each internal linear runs on NVFP4 or INT8
  * activations against 4-bit (NVFP4) weights.

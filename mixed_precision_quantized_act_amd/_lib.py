@@ -39,6 +39,10 @@ _SIGS = {
                                      ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
     "qlinear_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                     ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
+    "qlinear_nvfp4_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int,
+                                       _P, _P, _P, _P, _SZ, _P]),
+    "qlinear_int8_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P,
+                                      _P, _P, _P, _SZ, _P]),
     "qlinear_layer_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _I64, _I64,
                                _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
@@ -140,6 +144,22 @@ def qlinear_int8(a_q, a_s, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, 
     _check("qlinear_int8", lib().qlinear_int8(
         _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), _ptr(y),
         ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def qlinear_nvfp4_q(a_q, a_s, a_ts, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bias=None,
+                    epi=EPI_NONE, ws=None, stream=None):
+    """NVFP4 linear with the output quantized to NVFP4 (given tensor scale y_ts)."""
+    _check("qlinear_nvfp4_q", lib().qlinear_nvfp4_q(
+        _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias),
+        epi, _ptr(y_ts), _ptr(y_q), _ptr(y_s), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def qlinear_int8_q(a_q, a_s, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bias=None, epi=EPI_NONE,
+                   ws=None, stream=None):
+    """INT8 linear with the output quantized to NVFP4 (given tensor scale y_ts)."""
+    _check("qlinear_int8_q", lib().qlinear_int8_q(
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), epi,
+        _ptr(y_ts), _ptr(y_q), _ptr(y_s), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def qlinear_layer_workspace(fmt, M, N, K):

@@ -160,6 +160,66 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
       launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, stream));
 }
 
+// NVFP4 output of the linear (activation quantization of its consumer,
+// fused into the producing GEMM's epilogue)
+static int check_qout(int64_t M, int64_t N, int64_t K, qa_epi epi, const float* y_ts,
+                      const uint8_t* y_q, const uint8_t* y_s) {
+  if (int s = check_mk(M, K)) return s;
+  if (N < 0 || N >= kMaxDim || N % 16) return QA_ESHAPE;
+  if (int s = check_out(QA_OUT_BF16, epi)) return s;
+  if (!y_ts || !y_q || !y_s) return QA_EINVAL;
+  if (!aligned16(y_q)) return QA_EALIGN;
+  return QA_OK;
+}
+
+static bool qout_aliases(const uint8_t* y_q, const uint8_t* y_s, int64_t M, int64_t N,
+                         const void* a, size_t an, const void* w, size_t wn, const void* ws,
+                         size_t ws_bytes) {
+  const size_t qb = (size_t)(M * N / 2), sb = (size_t)(M * N / 16);
+  return overlap(y_q, qb, y_s, sb) || overlap(y_q, qb, a, an) || overlap(y_s, sb, a, an) ||
+         overlap(y_q, qb, w, wn) || overlap(y_s, sb, w, wn) || overlap(y_q, qb, ws, ws_bytes) ||
+         overlap(y_s, sb, ws, ws_bytes);
+}
+
+int qlinear_nvfp4_q(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                    const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M,
+                    int64_t N, int64_t K, const uint16_t* bias, qa_epi epi, const float* y_ts,
+                    uint8_t* y_q, uint8_t* y_s, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !a_s || !a_ts || !w_q || !w_s || !w_ts) return QA_EINVAL;
+  if (int s = check_qout(M, N, K, epi, y_ts, y_q, y_s)) return s;
+  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  {
+    const size_t need = nvfp4_gemm_ws_need(M, N, K, w_s);
+    if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
+  }
+  if (!aligned16(ws)) return QA_EALIGN;
+  if (qout_aliases(y_q, y_s, M, N, a_q, (size_t)(M * K / 2), w_q, (size_t)(N * K / 2), ws,
+                   ws_bytes))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  GemmOut o = {nullptr, N, 0, epi == QA_EPI_GELU_TANH, bias, y_q, y_s, y_ts};
+  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+}
+
+int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
+                   const float* w_ts, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                   qa_epi epi, const float* y_ts, uint8_t* y_q, uint8_t* y_s, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !a_s || !w_q || !w_s || !w_ts) return QA_EINVAL;
+  if (int s = check_qout(M, N, K, epi, y_ts, y_q, y_s)) return s;
+  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  {
+    const size_t need = int8_gemm_ws_need(M, N, K, w_s);
+    if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
+  }
+  if (!aligned16(ws)) return QA_EALIGN;
+  if (qout_aliases(y_q, y_s, M, N, a_q, (size_t)(M * K), w_q, (size_t)(N * K / 2), ws, ws_bytes))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  GemmOut o = {nullptr, N, 0, epi == QA_EPI_GELU_TANH, bias, y_q, y_s, y_ts};
+  return hip_status(launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+}
+
 size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0) return 0;
   if (fmt == QA_NVFP4)

@@ -25,6 +25,9 @@ struct GemmOut {
   int out_f32;            // 0: bf16, 1: f32
   int gelu;               // 0: none, 1: GELU-tanh
   const uint16_t* bias;   // bf16 [N] or null
+  uint8_t* yq = nullptr;  // non-null: NVFP4 output (codes [M][N/2], scales [M][N/16])
+  uint8_t* ys = nullptr;  //   quantized with the given tensor scale *y_ts instead of y
+  const float* y_ts = nullptr;
 };
 size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,

@@ -136,7 +136,24 @@ struct EpiArgs {
   const uint16_t* bias;
   int64_t M, N;
   int vec_ok;            // y 16-byte aligned and ldy % 4 == 0: vector stores
+  uint8_t* yq;           // NVFP4 output: codes [M][N/2], scales [M][N/16],
+  uint8_t* ys;           // with the given tensor scale *y_ts
+  const float* y_ts;
 };
+
+// Epilogue kinds (one kernel each, so that the executed epilogue code stays
+// compact): bf16 output with 16-byte aligned rows staged through LDS (no
+// bias or GELU, bias, GELU, both); any output stored from registers;
+// NVFP4-quantized output.
+enum {
+  kEpiPlain = 0,
+  kEpiGeneral = 1,
+  kEpiQuant = 2,
+  kEpiStagedBias = 3,
+  kEpiStagedGelu = 4,
+  kEpiStagedBiasGelu = 5
+};
+__host__ __device__ constexpr bool epi_staged(int k) { return k == kEpiPlain || k >= kEpiStagedBias; }
 
 // ---------------------------------------------------------------- GEMM --
 
@@ -227,10 +244,7 @@ struct RawWords<true> {
   typedef u32x4 A;       // INT8: the lane's 16 bytes of a row's stage
 };
 
-// kPlain: bf16 output, 16-byte aligned rows, no bias, no GELU (the
-// epilogue stages tiles through LDS); otherwise a general epilogue stores
-// from registers.  Two kernels keep the executed epilogue code compact.
-template <bool I8, bool kPlain>
+template <bool I8, int kEpi>
 __global__ void __launch_bounds__(kThreads, 1)
 qgemm_kernel(GemmArgs g, EpiArgs e) {
   using R = Raw<I8>;
@@ -443,7 +457,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   float row_scale[kFM];
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
-    row_scale[i] = I8 && kPlain ? g.a_rs[min<int64_t>(m0 + wm * 128 + 32 * i + (lane & 31), e.M - 1)]
+    row_scale[i] = I8 && epi_staged(kEpi) ? g.a_rs[min<int64_t>(m0 + wm * 128 + 32 * i + (lane & 31), e.M - 1)]
                                 : 1.0f;
 
   // ---- pipeline.  Units are issued in order, one per two stages, with
@@ -510,15 +524,28 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   float rs[kFM];
 #pragma unroll
   for (int i = 0; i < kFM; ++i) {
-    if constexpr (I8 && !kPlain)       // (the general kernel reads them here)
+    if constexpr (I8 && !epi_staged(kEpi))   // (the other kernels read them here)
       row_scale[i] = g.a_rs[min<int64_t>(wave_row0 + 32 * i + c, e.M - 1)];
     rs[i] = I8 ? row_scale[i] * alpha : alpha;
   }
-  if constexpr (kPlain) {
+  if constexpr (epi_staged(kEpi)) {
     // bf16 staged per 32-row slice through this wave's own 8 KB of the idle
     // ring -- rows of 256 bytes, 16-byte chunk k of row r at slot k ^ (r &
     // 15) -- and stored as 4 rows x 256 contiguous bytes per instruction
+    constexpr bool kBias = kEpi == kEpiStagedBias || kEpi == kEpiStagedBiasGelu;
+    constexpr bool kGelu = kEpi == kEpiStagedGelu || kEpi == kEpiStagedBiasGelu;
     uint8_t* const stg = smem + wave * 8192;
+    // bias of the lane's 64 columns (columns past N read column N-1)
+    float bv[kBias ? kFN : 1][4][4];
+    if constexpr (kBias)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            bv[j][q][t] = __uint_as_float(
+                (uint32_t)e.bias[min<int64_t>(wave_col0 + 32 * j + 8 * q + 4 * lh + t, e.N - 1)] << 16);
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
 #pragma unroll
@@ -526,9 +553,15 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x16& a = acc[i][j];
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[t] = a[4 * q + t] * rs[i];
+            if constexpr (kBias) v[t] += bv[j][q][t];
+            if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
+          }
           *reinterpret_cast<u32x2*>(stg + c * 256 + (((4 * j + q) ^ (c & 15)) << 4) + 8 * lh) =
-              u32x2{bf16_pack(a[4 * q] * rs[i], a[4 * q + 1] * rs[i]),
-                    bf16_pack(a[4 * q + 2] * rs[i], a[4 * q + 3] * rs[i])};
+              u32x2{bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3])};
         }
       // a wave's LDS operations run in order, so the reads below see these
       // writes without a wait; the fence only keeps the compiler's order
@@ -561,6 +594,70 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       // the next pass overwrites the slice after these reads (in order)
       asm volatile("" ::: "memory");
     }
+  } else if constexpr (kEpi == kEpiQuant) {
+    // NVFP4 output with the given tensor scale s_T: every output is rounded
+    // to bf16 and goes through the encoder's arithmetic (16-column groups
+    // along the row, E4M3 scale from the group's |max|, E2M1 codes), so the
+    // codes equal act_quant (given s_T) of the bf16 output.  In 32-column
+    // block j, group p holds columns 16p .. 16p+15: lane (h, c) owns its
+    // columns 4h .. 4h+3 (q = 2p) and 8+4h .. 8+4h+3 (q = 2p+1).  The two
+    // lanes of a group (c and c+32) exchange their maxima and their code
+    // halves; lane h stores code bytes 4h .. 4h+3 of the group's 8 and lane
+    // 0 of the pair the scale byte.  (Staging these small stores through
+    // LDS into whole row segments measured slower.)
+    const float s_t = *e.y_ts;
+    const float gsc = recip0(6.0f * s_t);
+    const int64_t cpr = e.N / 2, spr = e.N / 16;       // code and scale bytes per row
+    auto store = [&](auto has_bias, auto has_gelu) {
+      constexpr bool kBias = decltype(has_bias)::value, kGelu = decltype(has_gelu)::value;
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int64_t col0 = wave_col0 + j * 32 + p * 16;   // the group's first column
+          float bv[8];
+          if constexpr (kBias)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              bv[t] = __uint_as_float(
+                  (uint32_t)e.bias[min<int64_t>(col0 + 8 * (t >> 2) + 4 * lh + (t & 3), e.N - 1)] << 16);
+#pragma unroll
+          for (int i = 0; i < kFM; ++i) {
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              v[t] = acc[i][j][4 * (2 * p + (t >> 2)) + (t & 3)] * rs[i];
+              if constexpr (kBias) v[t] += bv[t];
+              if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
+            }
+            const u32x4 w = {bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3]), bf16_pack(v[4], v[5]),
+                             bf16_pack(v[6], v[7])};
+            uint32_t mx = fold_max(abs_max8_pk(w, u16x2{0, 0}));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+            const uint32_t enc = e4m3_encode(__uint_as_float(mx << 16) * gsc);
+            const float inv = recip0(e4m3_decode(enc) * s_t);
+            const uint32_t own = e2m1_pack8(w, inv);
+            const uint32_t other = (uint32_t)__shfl_xor((int)own, 32);
+            const uint32_t word = lh == 0 ? ((own & 0xFFFFu) | (other << 16))
+                                          : ((other >> 16) | (own & 0xFFFF0000u));
+            const int64_t row = wave_row0 + i * 32 + c;
+            if (row < e.M && col0 < e.N) {
+              *reinterpret_cast<uint32_t*>(e.yq + row * cpr + col0 / 2 + 4 * lh) = word;
+              if (lh == 0) e.ys[row * spr + col0 / 16] = (uint8_t)enc;
+            }
+          }
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    if (e.bias && e.gelu)
+      store(T(), T());
+    else if (e.bias)
+      store(T(), F());
+    else if (e.gelu)
+      store(F(), T());
+    else
+      store(F(), F());
   } else {
     // general: from registers, 4 consecutive outputs per lane and (i, j, q)
     auto store = [&](auto has_bias, auto has_gelu) {
@@ -670,32 +767,41 @@ static hipError_t launch_scale_tiles(const uint8_t* s0, int64_t rows0, uint32_t*
   return hipGetLastError();
 }
 
-template <bool I8, bool kPlain>
+template <bool I8, int kEpi>
 static void launch_one(int grid, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
   if (g_ev_before || g_ev_after)
     // the events take the dispatch's own start and end timestamps: no
     // marker packets are added to the stream around the kernel
-    hipExtLaunchKernelGGL((qgemm_kernel<I8, kPlain>), dim3(grid), dim3(kThreads), 0, st,
+    hipExtLaunchKernelGGL((qgemm_kernel<I8, kEpi>), dim3(grid), dim3(kThreads), 0, st,
                           g_ev_before, g_ev_after, 0u, g, e);
   else
-    hipLaunchKernelGGL((qgemm_kernel<I8, kPlain>), dim3(grid), dim3(kThreads), 0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<I8, kEpi>), dim3(grid), dim3(kThreads), 0, st, g, e);
 }
 
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
   const int total = g.mt * g.nt;
   const int grid = 8 * ((total + 7) / 8);
-  const bool plain = !e.out_f32 && e.vec_ok && !e.bias && !e.gelu;
-  if (i8) {
-    if (plain)
-      launch_one<true, true>(grid, g, e, st);
-    else
-      launch_one<true, false>(grid, g, e, st);
-  } else {
-    if (plain)
-      launch_one<false, true>(grid, g, e, st);
-    else
-      launch_one<false, false>(grid, g, e, st);
-  }
+  int kind = kEpiGeneral;
+  if (e.yq)
+    kind = kEpiQuant;
+  else if (!e.out_f32 && e.vec_ok)
+    kind = e.bias ? (e.gelu ? kEpiStagedBiasGelu : kEpiStagedBias)
+                  : (e.gelu ? kEpiStagedGelu : kEpiPlain);
+  auto go = [&](auto i8c) {
+    constexpr bool I8 = decltype(i8c)::value;
+    switch (kind) {
+      case kEpiPlain: launch_one<I8, kEpiPlain>(grid, g, e, st); break;
+      case kEpiStagedBias: launch_one<I8, kEpiStagedBias>(grid, g, e, st); break;
+      case kEpiStagedGelu: launch_one<I8, kEpiStagedGelu>(grid, g, e, st); break;
+      case kEpiStagedBiasGelu: launch_one<I8, kEpiStagedBiasGelu>(grid, g, e, st); break;
+      case kEpiQuant: launch_one<I8, kEpiQuant>(grid, g, e, st); break;
+      default: launch_one<I8, kEpiGeneral>(grid, g, e, st); break;
+    }
+  };
+  if (i8)
+    go(std::true_type());
+  else
+    go(std::false_type());
   return hipGetLastError();
 }
 
@@ -727,7 +833,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
   g.b = w_q;
   g.a_ts = a_ts;
   g.w_ts = w_ts;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts};
   return launch_gemm(false, g, e, st);
 }
 
@@ -749,7 +855,7 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
   g.b = w_q;
   g.w_ts = w_ts;
   g.a_rs = a_s;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o)};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts};
   return launch_gemm(true, g, e, st);
 }
 

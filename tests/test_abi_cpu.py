@@ -168,3 +168,21 @@ def test_rel_err_validation():
     assert _status("rel_err", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
     assert _status("rel_err", FAKE, FAKE, 64, FAKE, None, 0, None) == -5
     assert _status("rel_err", FAKE, FAKE_ODD, 64, FAKE, FAKE, 1 << 20, None) == -3
+
+
+def test_quantized_output_validation():
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    yq, ys = ctypes.c_void_p(0x900000), ctypes.c_void_p(0xA00000)
+    big = 1 << 40
+    # N must be a multiple of 16 (whole NVFP4 groups)
+    assert _status("qlinear_nvfp4_q", *ok, 4, 24, 16, None, 0, FAKE, yq, ys, FAKE, big, None) == -2
+    # a tensor scale and both outputs are required; codes 16-byte aligned
+    assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, None, yq, ys, FAKE, big, None) == -1
+    assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, FAKE, None, ys, FAKE, big, None) == -1
+    assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, FAKE, ctypes.c_void_p(0x900004), ys,
+                   FAKE, big, None) == -3
+    assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 7, FAKE, yq, ys, FAKE, big, None) == -1
+    # codes overlapping the scales
+    assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, FAKE, yq, ctypes.c_void_p(0x900008),
+                   FAKE, big, None) == -7
+    assert _status("qlinear_int8_q", *ok[:5], 4, 32, 16, None, 0, FAKE, yq, ys, FAKE, 0, None) == -5

@@ -306,3 +306,84 @@ def test_scale_sources(path, where):
                         dev(np.array([wq[2]], np.float32)), y, M, N, K, ws=ws)
     t.cuda.synchronize()
     assert rel_fro(_out_host(y, False), _round_ref(ref, False)) <= TOL
+
+
+QOUT_SHAPES = [(300, 256, 128), (257, 160, 64), (33, 48, 1920), (130, 7680, 1920)]
+
+
+def _qout_case(path, M, N, K, bias, gelu, seed):
+    """Operands, oracle output Y (bf16 bits) and the given tensor scale."""
+    x, w = _case(M, N, K, seed=seed)
+    wq = Q.nvfp4_encode(w)
+    a = Q.nvfp4_encode(x) if path == "nvfp4" else Q.int8_encode(x)
+    ad = Q.nvfp4_decode(*a) if path == "nvfp4" else Q.int8_decode(*a)
+    b = F.f64_to_bf16_rne(np.random.default_rng(seed).standard_normal(N)) if bias else None
+    y = F.f64_to_bf16_rne(G.linear_ref(ad, Q.nvfp4_decode(*wq), b, gelu=gelu))
+    ts = Q.nvfp4_tensor_scale(y)
+    return a, wq, b, y, np.float32(ts)
+
+
+def _run_qout(path, a, wq, b, ts, M, N, K, gelu, fused):
+    """NVFP4 output through the fused epilogue, or through the bf16 output
+    and act_quant with the same given tensor scale."""
+    qa, t = _qa(), torch()
+    fmt = qa.NVFP4 if path == "nvfp4" else qa.INT8
+    ws = qa.workspace(qa.qlinear_workspace(fmt, M, N, K))
+    epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+    ts_d = dev(np.array([ts], np.float32))
+    yq = t.empty((M, N // 2), dtype=t.uint8, device="cuda")
+    ys = t.empty((M, N // 16), dtype=t.uint8, device="cuda")
+    bias = None if b is None else dev(b)
+    wts = dev(np.array([wq[2]], np.float32))
+    if fused:
+        if path == "nvfp4":
+            qa.qlinear_nvfp4_q(dev(a[0]), dev(a[1]), dev(np.array([a[2]], np.float32)), dev(wq[0]),
+                               dev(wq[1]), wts, ts_d, yq, ys, M, N, K, bias=bias, epi=epi, ws=ws)
+        else:
+            qa.qlinear_int8_q(dev(a[0]), dev(a[1]), dev(wq[0]), dev(wq[1]), wts, ts_d, yq, ys, M, N,
+                              K, bias=bias, epi=epi, ws=ws)
+    else:
+        y = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+        if path == "nvfp4":
+            qa.qlinear_nvfp4(dev(a[0]), dev(a[1]), dev(np.array([a[2]], np.float32)), dev(wq[0]),
+                             dev(wq[1]), wts, y, M, N, K, bias=bias, epi=epi, ws=ws)
+        else:
+            qa.qlinear_int8(dev(a[0]), dev(a[1]), dev(wq[0]), dev(wq[1]), wts, y, M, N, K,
+                            bias=bias, epi=epi, ws=ws)
+        qa.act_quant(qa.NVFP4, y.view(t.int16), yq, ys, ts_d, qa.TSCALE_GIVEN, None)
+    t.cuda.synchronize()
+    return host(yq), host(ys)
+
+
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+@pytest.mark.parametrize("M,N,K", QOUT_SHAPES)
+@pytest.mark.parametrize("bias,gelu", [(False, False), (True, True)])
+def test_quantized_output(path, M, N, K, bias, gelu):
+    # the fused NVFP4 output against the oracle: codes of the oracle's own
+    # bf16 output Y, quantized with the same given tensor scale.  The two Y
+    # agree to bf16 rounding (the 1e-3 bound above), so a few E2M1 codes sit
+    # on the other side of a rounding boundary and move by one code step
+    # (up to a third of their group's |max|): at least 99 % of the codes and
+    # scales are equal and the decoded outputs agree to 1e-2.  Against the
+    # unfused library path (bf16 output, then act_quant with the given
+    # scale), which sees the same bf16 values, the bytes are equal.
+    a, wq, b, y, ts = _qout_case(path, M, N, K, bias, gelu, seed=17)
+    codes, scales = _run_qout(path, a, wq, b, ts, M, N, K, gelu, fused=True)
+    oc, os_, _ = Q.nvfp4_encode(y, tscale=ts)
+    got = Q.nvfp4_decode(codes, scales, ts)
+    ref = Q.nvfp4_decode(oc, os_, ts)
+    assert np.mean(codes == oc) >= 0.99 and np.mean(scales == os_) >= 0.99
+    assert rel_fro(got, ref) <= 1e-2
+    uc, us = _run_qout(path, a, wq, b, ts, M, N, K, gelu, fused=False)
+    assert np.array_equal(codes, uc) and np.array_equal(scales, us)
+
+
+def test_quantized_output_saturating_scale():
+    # a given tensor scale far below the output's |max|: group scales and
+    # codes saturate (E4M3 448, E2M1 6) exactly as act_quant does
+    a, wq, b, y, ts = _qout_case("nvfp4", 64, 64, 64, False, False, seed=19)
+    small = np.float32(ts / 64)
+    codes, scales = _run_qout("nvfp4", a, wq, b, small, 64, 64, 64, False, fused=True)
+    uc, us = _run_qout("nvfp4", a, wq, b, small, 64, 64, 64, False, fused=False)
+    assert np.array_equal(codes, uc) and np.array_equal(scales, us)
+    assert np.any(scales == 0x7E)              # E4M3 448 reached
