@@ -61,6 +61,9 @@ static constexpr int kRawSlots = 4;
 #ifndef QACT_VALU_PER_MFMA
 #define QACT_VALU_PER_MFMA 5
 #endif
+#ifndef QACT_DS_READS
+#define QACT_DS_READS 0
+#endif
 static constexpr int kGroupM = QACT_GROUP_M;
 static constexpr int kFM = 4, kFN = 4;          // MFMA tiles per wave (rows, columns)
 
@@ -474,6 +477,11 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // under them.  The loop body has no branch, so that the accumulators
   // stay in the accumulation registers across it.
   const int nk = 2 * g.units;
+  // the raw-word reads of stage t+2 (NVFP4: 16, INT8: 12) go one per MFMA
+  // from the start of the stage: the scheduling template offers a read
+  // slot after every MFMA (measured 12 % faster for NVFP4 and 4 % for INT8
+  // than offering 8 slots)
+  constexpr int kDsReads = QACT_DS_READS > 0 ? QACT_DS_READS : 2 * kFM * kFN;
 #pragma unroll
   for (int u = 0; u < kRawSlots; ++u) issue_unit(u);
   wait_vm<3 * R::kLoads>();
@@ -493,7 +501,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
 #pragma unroll
     for (int i = 0; i < 2 * kFM * kFN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
-      if (i < 2 * kFM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+      if (i < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
       __builtin_amdgcn_sched_group_barrier(0x002, QACT_VALU_PER_MFMA, 0);   // VALU
     }
     pin_ops(nxt);
