@@ -112,12 +112,158 @@ def cpu_baseline(x, w, x_out, delta_prev, rows):
                       f"1 thread, float64 BLAS on {cores} threads; host has {os.cpu_count()} CPUs"}
 
 
+def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, steps=10,
+                  delta=0.05):
+    """The CogVideoX-2B-shaped stack (30 blocks; per block the four internal
+    linears QKV H->3H, O H->H, up H->F with GELU, down F->H; attention
+    replaced by its value slice, no token mixing) over `steps` drifting
+    timesteps, entirely through the library, in four modes: uniform W4A8,
+    uniform W4A4, DMPQ (masks from the previous step's Gamma, tau set once
+    so that half of the linears are INT8) and DMPQ + TDC.  Returns
+    ms/step (mean of steps 2..), the INT8 share and the skipped blocks."""
+    import math
+    import synth
+    J = 4
+    shapes = [(3 * H, H), (H, H), (F_, H), (H, F_)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1004)
+    layers = []
+    qw = qa.workspace(qa.act_quant_workspace(qa.NVFP4, F_, F_), dev)
+    for _ in range(L):
+        lay = []
+        for (N, K) in shapes:
+            w = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            q, sc, ts = qa.empty_nvfp4(N, K, dev)
+            qa.act_quant(qa.NVFP4, w.view(torch.int16), q, sc, ts, 0, qw)
+            lay.append((q, sc, ts, N, K))
+        layers.append(lay)
+    bf = torch.bfloat16
+    qkv = torch.empty((M, 3 * H), dtype=bf, device=dev)
+    o = torch.empty((M, H), dtype=bf, device=dev)
+    x1 = torch.empty((M, H), dtype=bf, device=dev)
+    u = torch.empty((M, F_), dtype=bf, device=dev)
+    dd = torch.empty((M, H), dtype=bf, device=dev)
+    a4 = qa.empty_nvfp4(M, F_, dev)
+    a8 = qa.empty_int8_act(M, F_, dev)
+    qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
+    gws = qa.workspace(max(qa.qlinear_workspace(f, M, N, K) for f in (qa.NVFP4, qa.INT8)
+                           for (N, K) in shapes), dev)
+    rws = qa.workspace(qa.reduce_workspace(M * H), dev)
+    ring = [[torch.empty((M, H), dtype=bf, device=dev) for _ in range(2)] for _ in range(L)]
+    sums = torch.zeros((L, 4), dtype=torch.float64, device=dev)
+    hsums = torch.zeros((L, 4), dtype=torch.float64).pin_memory()
+    alpha = np.full(L * J, 1.0, np.float32)
+    beta = np.full(L * J, 0.01, np.float32)
+    i16 = lambda t: t.view(torch.int16)
+
+    def linear(fmt, x, ldx, lay, y, gelu):
+        q, sc, ts, N, K = lay
+        xv = torch.as_strided(x, (M, K), (ldx, 1))
+        epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+        if fmt == 0:
+            aq = a4[0].view(-1)[: M * K // 2].view(M, K // 2)
+            asc = a4[1].view(-1)[: M * K // 16].view(M, K // 16)
+            qa.act_quant(qa.NVFP4, i16(xv), aq, asc, a4[2], 0, qws, M=M, K=K, ldx=ldx, stream=stream)
+            qa.qlinear_nvfp4(aq, asc, a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+        else:
+            aq = a8[0].view(-1)[: M * K].view(M, K)
+            qa.act_quant(qa.INT8, i16(xv), aq, a8[1], M=M, K=K, ldx=ldx, stream=stream)
+            qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+
+    # the drifting stack inputs x_t = bf16(x_{t-1} + 0.02 N(0,1)), made once
+    xs = []
+    x = synth.activations(4, M, H, "normal")
+    for t in range(steps):
+        x = synth.drift(4, t, x)
+        xs.append(torch.from_numpy(x.view(np.int16).copy()).to(dev).view(bf))
+
+    def run(mode, delta=delta):
+        last, n_stored = [1] * L, [0] * L
+        d_seen = []
+        computed_prev = np.zeros(L, np.uint8)
+        d_prev = np.full(L, math.inf)
+        gamma_prev, tau = None, None
+        times, int8_share, skipped = [], [], 0
+        for t in range(steps):
+            xd = xs[t]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "w4a8":
+                mask = np.ones(L * J, np.uint8)
+            elif mode == "w4a4":
+                mask = np.zeros(L * J, np.uint8)
+            else:
+                if gamma_prev is not None and tau is None:
+                    p = np.repeat(gamma_prev, J) * alpha.astype(np.float64) + beta
+                    srt = np.sort(p)
+                    tau = 0.5 * (srt[(len(p) - 1) // 2] + srt[len(p) // 2])
+                mask = qa.dmpq_mask(gamma_prev, alpha, beta, tau if tau is not None else 0.0, L, J)
+            skip = (qa.tdc_decide(t, d_prev, computed_prev, delta) if mode == "full"
+                    else np.zeros(L, np.uint8))
+            cur = xd
+            for l in range(L):
+                out = torch.empty_like(cur)
+                if skip[l]:
+                    qa.tdc_apply(i16(cur), i16(ring[l][last[l]]), i16(out), sums[l, :2], rws,
+                                 stream=stream)
+                    computed_prev[l] = 0
+                    skipped += 1
+                else:
+                    m = mask[l * J:(l + 1) * J]
+                    linear(m[0], cur, H, layers[l][0], qkv, False)
+                    linear(m[1], qkv.view(-1)[2 * H:], 3 * H, layers[l][1], o, False)
+                    qa.tdc_apply(i16(cur), i16(o), i16(x1), stream=stream)
+                    linear(m[2], x1, H, layers[l][2], u, True)
+                    linear(m[3], u, F_, layers[l][3], dd, False)
+                    qa.tdc_apply(i16(x1), i16(dd), i16(out), stream=stream)
+                    prev = ring[l][last[l]] if n_stored[l] else None
+                    nxt = last[l] ^ 1
+                    qa.tdc_update(i16(cur), i16(out), None if prev is None else i16(prev),
+                                  i16(ring[l][nxt]), sums[l], rws, stream=stream)
+                    last[l] = nxt
+                    n_stored[l] = min(n_stored[l] + 1, 2)
+                    computed_prev[l] = 1
+                cur = out
+            hsums.copy_(sums, non_blocking=True)
+            torch.cuda.current_stream(dev).synchronize()
+            hs = hsums.numpy()
+            gamma_prev = np.array([qa.gamma_from_sums(hs[l, :2]) for l in range(L)])
+            for l in range(L):
+                if not skip[l]:
+                    d_prev[l] = qa.rel_l2_from_sums(hs[l]) if n_stored[l] > 1 else math.inf
+                    if n_stored[l] > 1:
+                        d_seen.append(d_prev[l])
+            times.append(time.perf_counter() - t0)
+            int8_share.append(float(mask.mean()))
+        return {"ms_per_step": round(1e3 * float(np.mean(times[2:])), 2),
+                "int8_share": round(float(np.mean(int8_share[2:])), 3),
+                "skipped_blocks": int(skipped), "blocks_run": L * steps, "delta": delta,
+                "d_median": round(float(np.median(d_seen)), 4) if d_seen else None}
+
+    res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full")}
+    # the synthetic trajectory's block updates change by d ~ d_median from
+    # step to step; a threshold at that median shows the skip path's speed
+    if res["dmpq"]["d_median"]:
+        res["full_delta_at_median_d"] = run("full", delta=res["dmpq"]["d_median"])
+    res["config"] = {"blocks": L, "hidden": H, "ffn": F_, "tokens": M, "steps": steps,
+                     "delta": delta, "alpha": 1.0, "beta": 0.01,
+                     "block": "QKV -> value slice -> O (+res) -> up+GELU -> down (+res); "
+                              "no attention mixing"}
+    res["full_vs_dmpq_speedup"] = round(res["dmpq"]["ms_per_step"] / res["full"]["ms_per_step"], 3)
+    if "full_delta_at_median_d" in res:
+        res["full_at_median_d_vs_dmpq_speedup"] = round(
+            res["dmpq"]["ms_per_step"] / res["full_delta_at_median_d"]["ms_per_step"], 3)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--stack-steps", type=int, default=10,
+                    help="timesteps of the 30-block stack section (0 skips it)")
     ap.add_argument("--cold-reps", type=int, default=9,
                     help="reps of each bandwidth kernel timed after a 1 GiB cache-evicting read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -344,6 +490,8 @@ def main():
                  "unfused_TFLOP/s": round(2.0 * M * F_ * K / (t_un * 1e-6) / 1e12, 1),
                  "fused_TFLOP/s": round(2.0 * M * F_ * K / (t_fu * 1e-6) / 1e12, 1)}
     del h, hq, hs
+    stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
+             if args.stack_steps > 0 else None)
 
     ms_step = wall * 1e3 / args.steps
     flops_step = 2 * 2.0 * M * N * K
@@ -400,6 +548,7 @@ def main():
         "kernels": kern,
         "cold": cold,
         "ffn_up_fused_nvfp4_output": ffn_fused,
+        "stack_cogvideox2b_shape": stack,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -745,8 +745,11 @@ size_t int8_gemm_ws_bytes(int64_t, int64_t N, int64_t K) { return scale_tiles_by
 // whose raw loads already touch more rows per unit, measured about 5 %
 // slower reading either scale array in place than after one re-layout
 // launch of both, so it always takes the per-tile copies.
+#ifndef QACT_INT8_W_DIRECT
+#define QACT_INT8_W_DIRECT 1
+#endif
 static bool w_scales_direct(int64_t K, const void* w_s) {
-  return K % kUnitK == 0 && (reinterpret_cast<uintptr_t>(w_s) & 3) == 0;
+  return QACT_INT8_W_DIRECT && K % kUnitK == 0 && (reinterpret_cast<uintptr_t>(w_s) & 3) == 0;
 }
 
 size_t nvfp4_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void*) {
