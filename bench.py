@@ -177,9 +177,15 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
         x = synth.drift(4, t, x)
         xs.append(torch.from_numpy(x.view(np.int16).copy()).to(dev).view(bf))
 
-    def run(mode, delta=delta):
+    csums = torch.zeros((L, 3), dtype=torch.float64, device=dev)
+    hcsums = torch.zeros((L, 3), dtype=torch.float64).pin_memory()
+
+    def run(mode, delta=delta, cos_rule=False, cos_probe=False):
+        """cos_rule: skip on the cosine of the last two Deltas (> delta);
+        cos_probe: record those cosines (DMPQ only, no skips)."""
         last, n_stored = [1] * L, [0] * L
-        d_seen = []
+        d_seen, cos_seen = [], []
+        cos_prev = np.full(L, -1.0)
         computed_prev = np.zeros(L, np.uint8)
         d_prev = np.full(L, math.inf)
         gamma_prev, tau = None, None
@@ -198,8 +204,12 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                     srt = np.sort(p)
                     tau = 0.5 * (srt[(len(p) - 1) // 2] + srt[len(p) // 2])
                 mask = qa.dmpq_mask(gamma_prev, alpha, beta, tau if tau is not None else 0.0, L, J)
-            skip = (qa.tdc_decide(t, d_prev, computed_prev, delta) if mode == "full"
-                    else np.zeros(L, np.uint8))
+            if mode != "full":
+                skip = np.zeros(L, np.uint8)
+            elif cos_rule:
+                skip = qa.tdc_decide_cos(t, cos_prev, computed_prev, delta)
+            else:
+                skip = qa.tdc_decide(t, d_prev, computed_prev, delta)
             cur = xd
             for l in range(L):
                 out = torch.empty_like(cur)
@@ -220,13 +230,22 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                     nxt = last[l] ^ 1
                     qa.tdc_update(i16(cur), i16(out), None if prev is None else i16(prev),
                                   i16(ring[l][nxt]), sums[l], rws, stream=stream)
+                    if (cos_rule or cos_probe) and prev is not None:
+                        qa.delta_cosine(i16(ring[l][nxt]), i16(prev), csums[l], rws, stream=stream)
                     last[l] = nxt
                     n_stored[l] = min(n_stored[l] + 1, 2)
                     computed_prev[l] = 1
                 cur = out
             hsums.copy_(sums, non_blocking=True)
+            if cos_rule or cos_probe:
+                hcsums.copy_(csums, non_blocking=True)
             torch.cuda.current_stream(dev).synchronize()
             hs = hsums.numpy()
+            if cos_rule or cos_probe:
+                for l in range(L):
+                    if not skip[l] and n_stored[l] > 1:
+                        cos_prev[l] = qa.cosine_from_sums(hcsums.numpy()[l])
+                        cos_seen.append(cos_prev[l])
             gamma_prev = np.array([qa.gamma_from_sums(hs[l, :2]) for l in range(L)])
             for l in range(L):
                 if not skip[l]:
@@ -238,13 +257,19 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
         return {"ms_per_step": round(1e3 * float(np.mean(times[2:])), 2),
                 "int8_share": round(float(np.mean(int8_share[2:])), 3),
                 "skipped_blocks": int(skipped), "blocks_run": L * steps, "delta": delta,
-                "d_median": round(float(np.median(d_seen)), 4) if d_seen else None}
+                "d_median": round(float(np.median(d_seen)), 4) if d_seen else None,
+                "cos_median": round(float(np.median(cos_seen)), 4) if cos_seen else None}
 
     res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full")}
     # the synthetic trajectory's block updates change by d ~ d_median from
     # step to step; a threshold at that median shows the skip path's speed
     if res["dmpq"]["d_median"]:
         res["full_delta_at_median_d"] = run("full", delta=res["dmpq"]["d_median"])
+    # the cosine rule of Fig. 4 (a variant): threshold at the median cosine
+    # of the DMPQ run's successive Deltas (an untimed probe run)
+    probe = run("dmpq", cos_probe=True)
+    if probe["cos_median"] is not None:
+        res["full_cos_at_median"] = run("full", delta=probe["cos_median"], cos_rule=True)
     res["config"] = {"blocks": L, "hidden": H, "ffn": F_, "tokens": M, "steps": steps,
                      "delta": delta, "alpha": 1.0, "beta": 0.01,
                      "block": "QKV -> value slice -> O (+res) -> up+GELU -> down (+res); "
@@ -253,6 +278,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     if "full_delta_at_median_d" in res:
         res["full_at_median_d_vs_dmpq_speedup"] = round(
             res["dmpq"]["ms_per_step"] / res["full_delta_at_median_d"]["ms_per_step"], 3)
+    if "full_cos_at_median" in res:
+        res["full_cos_vs_dmpq_speedup"] = round(
+            res["dmpq"]["ms_per_step"] / res["full_cos_at_median"]["ms_per_step"], 3)
     return res
 
 

@@ -202,6 +202,17 @@ int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t 
 int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2,
             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* delta_cosine (Fig. 4 caption: the agreement of a block's successive
+ * residual updates Delta_t and Delta_{t-1}, shown as cosine similarity
+ * beside the relative L2 difference):  sums3 = { sum d_new d_prev,
+ * sum d_new^2, sum d_prev^2 } over bf16 [n] device arrays, float64 device
+ * output (exact terms, fixed-order sums); the cosine is
+ * sums3[0] / (sqrt(sums3[1]) sqrt(sums3[2])) (qa_cosine_from_sums; 0 when
+ * either norm is 0).  Workspace: reduce_workspace(n) bytes; sums3 must not
+ * lie in it. */
+int delta_cosine(const uint16_t* d_new, const uint16_t* d_prev, int64_t n, double* sums3,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Host-side decisions (pure functions on HOST arrays; no GPU work).
  *
@@ -234,6 +245,12 @@ int dmpq_fit(const double* gamma, const double* erel, int T, int L, int J, float
              float* beta);
 int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
                double delta, uint8_t* skip);
+/* tdc_decide_cos: the same rule with the cosine of Fig. 4 as the agreement
+ * measure (a page variant of the relative-L2 rule):
+ *   skip[l] = t >= 2 && computed_prev[l] && cos_prev[l] > threshold,
+ * cos_prev[l] the cosine of the block's last two Deltas (delta_cosine). */
+int tdc_decide_cos(int t, const double* cos_prev, const uint8_t* computed_prev, int L,
+                   double threshold, uint8_t* skip);
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
  * inside qlinear) launches its main GEMM kernel with hipExtLaunchKernel so
  * that `before` and `after` take that dispatch's start and end timestamps
@@ -246,6 +263,7 @@ int qa_set_gemm_events(hipEvent_t before, hipEvent_t after);
 double qa_gamma_from_sums(const double* sums2);
 double qa_rel_l2_from_sums(const double* sums4);
 double qa_rel_err_from_sums(const double* sums2);
+double qa_cosine_from_sums(const double* sums3);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,9 @@ _SIGS = {
     "tdc_update": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_apply": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "rel_err": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "delta_cosine": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "tdc_decide_cos": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
+    "qa_cosine_from_sums": (ctypes.c_double, [_P]),
     "dmpq_fit": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]),
     "dmpq_mask": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_double, _P]),
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
@@ -207,6 +210,13 @@ def rel_err(y_q, y_ref, sums2, ws, n=None, stream=None):
                                     _nbytes(ws), _stream(stream)))
 
 
+def delta_cosine(d_new, d_prev, sums3, ws, n=None, stream=None):
+    """sums3 <- {sum d_new d_prev, sum d_new^2, sum d_prev^2} (bf16 device arrays)."""
+    n = d_new.numel() if n is None else n
+    _check("delta_cosine", lib().delta_cosine(_ptr(d_new), _ptr(d_prev), n, _ptr(sums3),
+                                              _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
 # ------------------------------------------------------- host decisions --
 
 def _host_array(a, dtype):
@@ -264,6 +274,28 @@ def dmpq_fit(gamma, erel, J):
     _check("dmpq_fit", lib().dmpq_fit(g.ctypes.data, e.ctypes.data, T, L, J, alpha.ctypes.data,
                                       beta.ctypes.data))
     return alpha, beta
+
+
+def tdc_decide_cos(t, cos_prev, computed_prev, threshold, out=None):
+    import numpy as np
+    c = _host_array(cos_prev, np.float64)
+    cp = _host_array(computed_prev, np.uint8)
+    if cp.size < c.size:
+        raise ValueError("tdc_decide_cos: computed_prev needs one entry per block")
+    skip = np.zeros(c.size, dtype=np.uint8) if out is None else out
+    if skip.dtype != np.uint8 or skip.size < c.size or not skip.flags.c_contiguous:
+        raise ValueError("tdc_decide_cos: out must be a contiguous uint8 array, one entry per block")
+    _check("tdc_decide_cos", lib().tdc_decide_cos(int(t), c.ctypes.data, cp.ctypes.data, c.size,
+                                                  float(threshold), skip.ctypes.data))
+    return skip
+
+
+def cosine_from_sums(sums3):
+    import numpy as np
+    s = _host_array(sums3, np.float64)
+    if s.size < 3:
+        raise ValueError("cosine_from_sums: needs the three sums")
+    return lib().qa_cosine_from_sums(s.ctypes.data)
 
 
 def set_gemm_events(before, after):

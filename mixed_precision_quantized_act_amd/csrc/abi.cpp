@@ -317,6 +317,14 @@ int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2
   return hip_status(launch_tdc(3, y_q, y_ref, nullptr, nullptr, n, sums2, ws, stream));
 }
 
+int delta_cosine(const uint16_t* d_new, const uint16_t* d_prev, int64_t n, double* sums3,
+                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!sums3) return QA_EINVAL;
+  if (int s = check_stream(d_new, d_prev, n, ws, ws_bytes, true)) return s;
+  if (overlap(sums3, 24, ws, ws_bytes)) return QA_EALIAS;
+  return hip_status(launch_tdc(4, d_new, d_prev, nullptr, nullptr, n, sums3, ws, stream));
+}
+
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
   set_gemm_events(before, after);
@@ -336,6 +344,20 @@ double qa_gamma_from_sums(const double* sums2) {
 
 double qa_rel_l2_from_sums(const double* sums4) {
   return sums4 ? ratio0(sqrt(sums4[2]), sqrt(sums4[3])) : NAN;
+}
+
+double qa_cosine_from_sums(const double* sums3) {
+  if (!sums3) return NAN;
+  const double den = sqrt(sums3[1]) * sqrt(sums3[2]);
+  return den == 0.0 ? 0.0 : sums3[0] / den;
+}
+
+int tdc_decide_cos(int t, const double* cos_prev, const uint8_t* computed_prev, int L,
+                   double threshold, uint8_t* skip) {
+  if (L < 0 || !skip || (L && t >= 2 && (!cos_prev || !computed_prev))) return QA_EINVAL;
+  for (int l = 0; l < L; ++l)
+    skip[l] = (uint8_t)(t >= 2 && computed_prev[l] && cos_prev[l] > threshold);
+  return QA_OK;
 }
 
 double qa_rel_err_from_sums(const double* sums2) {

@@ -45,7 +45,7 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 size_t reduce_ws_bytes(int64_t n);
-// mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err
+// mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* delta_prev,
                       uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream);
 

@@ -6,7 +6,9 @@
 // Delta = out - in and reuses it for invariant blocks (abstract), comparing
 // successive Deltas by relative L2 (Fig. 4 caption); E_rel, the layer-wise
 // relative quantization error that the DMPQ predictor is fitted to (Fig. 3
-// caption), is taken as the relative L2 error of the layer output.
+// caption), is taken as the relative L2 error of the layer output; the
+// cosine similarity of successive Deltas (Fig. 4 caption) is the other
+// agreement measure the pages show.
 //
 // tdc_apply may run in place (dst == in): every element is read and then
 // written by the same thread, so `in` and `dst` carry no restrict.
@@ -30,7 +32,7 @@ static constexpr int kRedBlocks = QACT_TDC_BLOCKS;
 static constexpr int kThreads = 256;
 static constexpr int kUnroll = QACT_TDC_UNROLL;
 
-enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3 };
+enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3, MODE_COS = 4 };
 
 struct Acc4 {
   double s[4];
@@ -41,6 +43,14 @@ __device__ __forceinline__ uint32_t tdc_pair(uint32_t xi, uint32_t bi, uint32_t 
   // xi, bi, pi: bf16 bit patterns (low 16 bits); returns the bf16 written
   const float x = __uint_as_float(xi << 16);
   const float b = __uint_as_float(bi << 16);
+  if (MODE == MODE_COS) {
+    // x = Delta_t, b = Delta_{t-1}: x b, x^2, b^2, each exact in float64
+    const double xd = (double)x, bd = (double)b;
+    a.s[0] = __fma_rn(xd, bd, a.s[0]);
+    a.s[1] = __fma_rn(xd, xd, a.s[1]);
+    a.s[2] = __fma_rn(bd, bd, a.s[2]);
+    return 0;
+  }
   if (MODE == MODE_RELERR) {
     // x = quantized output, b = reference: (x - b)^2 and b^2, each exact in
     // float64 (a bf16 difference has at most 17 significant bits)
@@ -105,7 +115,7 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
         const uint32_t hi = tdc_pair<MODE, PREV>(xv[u][i] >> 16, bv[u][i] >> 16, pv[u][i] >> 16, a);
         ov[i] = lo | (hi << 16);
       }
-      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && v < nvec)
+      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && MODE != MODE_COS && v < nvec)
         __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst) + v);
     }
   }
@@ -114,7 +124,7 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
     const int64_t e = nvec * 8 + threadIdx.x;
     if (e < n) {
       const uint32_t o = tdc_pair<MODE, PREV>(in[e], b[e], PREV ? prev[e] : 0u, a);
-      if (MODE != MODE_GAMMA && MODE != MODE_RELERR) dst[e] = (uint16_t)o;
+      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && MODE != MODE_COS) dst[e] = (uint16_t)o;
     }
   }
   if (!want_sums) return;
@@ -185,12 +195,15 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   else if (mode == MODE_APPLY)
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY, false>), g, t, 0, stream, in, b, prev, dst, n,
                        partial, want);
-  else
+  else if (mode == MODE_RELERR)
     hipLaunchKernelGGL((tdc_kernel<MODE_RELERR, false>), g, t, 0, stream, in, b, prev, dst, n,
+                       partial, want);
+  else
+    hipLaunchKernelGGL((tdc_kernel<MODE_COS, false>), g, t, 0, stream, in, b, prev, dst, n,
                        partial, want);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !want) return e;
-  const int ncols = mode == MODE_UPDATE ? 4 : 2;
+  const int ncols = mode == MODE_UPDATE ? 4 : mode == MODE_COS ? 3 : 2;
   hipLaunchKernelGGL(tdc_finalize_kernel, dim3(1), t, 0, stream, partial, (int)nb, ncols, sums);
   return hipGetLastError();
 }

@@ -28,6 +28,9 @@ Readings taken where the pages are silent:
     and measures d against the cached Delta it replaces.
   * Delta and outputs are bfloat16 rounded once (nearest-even) from the
     exact sum/difference; the norms are square roots of float64 sums.
+  * The cosine of Fig. 4 is <Delta_t, Delta_{t-1}> / (||Delta_t|| ||Delta_{t-1}||)
+    from float64 sums of exact terms (0 when either norm is 0); its skip
+    rule (a variant) is t >= 2, computed at t-1 and cos > threshold.
   * E_rel (the layer-wise relative quantization error of Fig. 3) is the
     relative L2 error ||Y_q - Y||_2 / ||Y||_2 of a linear's bf16 output
     against the bf16 output of the unquantized linear (0/0 = 0, x/0 = inf).
@@ -163,6 +166,28 @@ def rel_err_sums(yq_bits, yref_bits):
 def rel_err(s0, s1):
     """E_rel = sqrt(s0) / sqrt(s1) from the two sums."""
     return ratio(math.sqrt(s0), math.sqrt(s1))
+
+
+def cosine_sums(new_bits, prev_bits):
+    """(sum new*prev, sum new^2, sum prev^2), each correctly rounded."""
+    a = bf16_to_f64(new_bits).ravel()
+    b = bf16_to_f64(prev_bits).ravel()
+    return _fsum(a * b), _fsum(a * a), _fsum(b * b)
+
+
+def cosine(s0, s1, s2):
+    """Cosine similarity from the three sums (0 when a norm is 0)."""
+    den = math.sqrt(s1) * math.sqrt(s2)
+    return 0.0 if den == 0.0 else s0 / den
+
+
+def tdc_decide_cos(t, cos_prev, computed_prev, threshold):
+    """skip[l] = t >= 2 and computed_prev[l] and cos_prev[l] > threshold."""
+    c = np.asarray(cos_prev, dtype=np.float64)
+    computed_prev = np.asarray(computed_prev).astype(bool)
+    if t < 2:
+        return np.zeros(c.shape, dtype=np.uint8)
+    return (computed_prev & (c > float(threshold))).astype(np.uint8)
 
 
 def fraction_to_f32(q):

@@ -186,3 +186,19 @@ def test_quantized_output_validation():
     assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, FAKE, yq, ctypes.c_void_p(0x900008),
                    FAKE, big, None) == -7
     assert _status("qlinear_int8_q", *ok[:5], 4, 32, 16, None, 0, FAKE, yq, ys, FAKE, 0, None) == -5
+
+
+def test_cosine_helpers_match_oracle():
+    from oracle import tdc as T
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        s = np.array([rng.standard_normal(), abs(rng.standard_normal()), abs(rng.standard_normal())])
+        assert qa.cosine_from_sums(s) == T.cosine(*s)
+    assert qa.cosine_from_sums(np.array([1.0, 0.0, 4.0])) == 0.0
+    for t in (0, 1, 2, 7):
+        c = rng.uniform(0.8, 1.0, 9)
+        cp = rng.integers(0, 2, 9)
+        np.testing.assert_array_equal(qa.tdc_decide_cos(t, c, cp, 0.9),
+                                      T.tdc_decide_cos(t, c, cp, 0.9))
+    assert _status("delta_cosine", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
+    assert _status("delta_cosine", FAKE, FAKE, 64, FAKE, None, 0, None) == -5

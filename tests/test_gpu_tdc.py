@@ -198,3 +198,30 @@ def test_rel_err_worked_example():
     got = gpu_rel_err(q, r)
     assert list(got) == [1.0, 25.0]
     assert _qa().rel_err_from_sums(got) == 0.2
+
+
+def gpu_cosine(a, b):
+    qa, t = _qa(), torch()
+    sums = t.zeros(3, dtype=t.float64, device="cuda")
+    ws = qa.workspace(qa.reduce_workspace(len(a)))
+    qa.delta_cosine(dev(a), dev(b), sums, ws)
+    t.cuda.synchronize()
+    return host(sums)
+
+
+@pytest.mark.parametrize("n", [65536, 8, 13, 1, 1000003])
+def test_delta_cosine(n):
+    a, b = pair(n, seed=37, scale=0.2)
+    got = gpu_cosine(a, b)
+    want = T.cosine_sums(a, b)
+    _close(got, want)
+    qa = _qa()
+    assert abs(qa.cosine_from_sums(got) - T.cosine(*want)) <= 1e-12
+
+
+def test_delta_cosine_worked_example():
+    v = F.f64_to_bf16_rne(np.array([3.0, 4.0] + [0.0] * 14))
+    e1 = F.f64_to_bf16_rne(np.array([1.0] + [0.0] * 15))
+    got = gpu_cosine(e1, v)
+    assert list(got) == [3.0, 1.0, 25.0]
+    assert _qa().cosine_from_sums(got) == 0.6

@@ -259,3 +259,36 @@ def test_calibrate_time_shift():
     e2[3, 0] = np.inf
     a2, _ = T.calibrate(g, e2, J)
     assert abs(float(a2[0]) - 3.0) <= 4e-7 * 3
+
+
+# ---- cosine similarity of successive Deltas (Fig. 4 caption) ----
+
+def test_cosine_worked_values():
+    e1 = F.f64_to_bf16_rne(np.array([1.0, 0.0, 0.0, 0.0]))
+    e2 = F.f64_to_bf16_rne(np.array([0.0, 2.0, 0.0, 0.0]))
+    v = F.f64_to_bf16_rne(np.array([3.0, 4.0, 0.0, 0.0]))
+    assert T.cosine(*T.cosine_sums(e1, e2)) == 0.0                     # orthogonal
+    assert T.cosine(*T.cosine_sums(v, v)) == 1.0                       # identical
+    neg = F.f64_to_bf16_rne(-F.bf16_to_f64(v))
+    assert T.cosine(*T.cosine_sums(v, neg)) == -1.0                    # opposite
+    assert T.cosine(*T.cosine_sums(e1, v)) == 0.6                      # 3/5
+    z = F.f64_to_bf16_rne(np.zeros(4))
+    assert T.cosine(*T.cosine_sums(v, z)) == 0.0                       # zero norm
+
+
+def test_cosine_matches_numpy_and_scale_invariance():
+    rng = np.random.default_rng(5)
+    a = F.f64_to_bf16_rne(rng.standard_normal(777))
+    b = F.f64_to_bf16_rne(F.bf16_to_f64(a) + 0.3 * rng.standard_normal(777))
+    af, bf = F.bf16_to_f64(a), F.bf16_to_f64(b)
+    want = float(af @ bf / (np.linalg.norm(af) * np.linalg.norm(bf)))
+    got = T.cosine(*T.cosine_sums(a, b))
+    assert abs(got - want) <= 1e-14
+    b4 = F.f64_to_bf16_rne(4.0 * bf)                                   # exact scaling
+    assert abs(T.cosine(*T.cosine_sums(a, b4)) - got) <= 1e-15
+
+
+def test_decide_cos_rule():
+    assert list(T.tdc_decide_cos(1, [0.99, 0.99], [1, 1], 0.9)) == [0, 0]   # warm-up
+    assert list(T.tdc_decide_cos(2, [0.99, 0.9, 0.5], [1, 1, 1], 0.9)) == [1, 0, 0]  # strict
+    assert list(T.tdc_decide_cos(5, [0.99, 0.99], [0, 1], 0.9)) == [0, 1]   # after a skip
