@@ -64,6 +64,11 @@ static constexpr int kRawSlots = 4;
 #ifndef QACT_DS_READS
 #define QACT_DS_READS 0
 #endif
+#ifndef QACT_EPI_ROWS
+#define QACT_EPI_ROWS 32
+#endif
+// rows of a wave's output staged per pass of the bf16 epilogue
+static constexpr int kPassTiles = QACT_EPI_ROWS / 32;
 static constexpr int kGroupM = QACT_GROUP_M;
 static constexpr int kFM = 4, kFN = 4;          // MFMA tiles per wave (rows, columns)
 
@@ -79,8 +84,8 @@ struct Raw {
   static constexpr int kSmem = kRawSlots * kSlot;
   static constexpr int kLoads = I8 ? 7 : 6;     // DMA instructions per wave per unit
 };
-// the epilogue stages 32 rows x 128 bf16 per wave through the idle ring
-static_assert(Raw<false>::kSmem >= 4 * 8192, "epilogue staging");
+// the epilogue stages (32 kPassTiles) rows x 128 bf16 per wave through the idle ring
+static_assert(Raw<false>::kSmem >= 4 * 8192 * kPassTiles, "epilogue staging");
 static_assert(Raw<true>::kSmem <= 160 * 1024, "LDS");
 
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -542,7 +547,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     // 15) -- and stored as 4 rows x 256 contiguous bytes per instruction
     constexpr bool kBias = kEpi == kEpiStagedBias || kEpi == kEpiStagedBiasGelu;
     constexpr bool kGelu = kEpi == kEpiStagedGelu || kEpi == kEpiStagedBiasGelu;
-    uint8_t* const stg = smem + wave * 8192;
+    uint8_t* const stg = smem + wave * 8192 * kPassTiles;
     // bias of the lane's 64 columns (columns past N read column N-1)
     float bv[kBias ? kFN : 1][4][4];
     if constexpr (kBias)
@@ -555,40 +560,44 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
             bv[j][q][t] = __uint_as_float(
                 (uint32_t)e.bias[min<int64_t>(wave_col0 + 32 * j + 8 * q + 4 * lh + t, e.N - 1)] << 16);
 #pragma unroll
-    for (int i = 0; i < kFM; ++i) {
+    for (int pi = 0; pi < kFM; pi += kPassTiles) {
 #pragma unroll
-      for (int j = 0; j < kFN; ++j)
+      for (int ii = 0; ii < kPassTiles; ++ii) {
+        const int i = pi + ii;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16& a = acc[i][j];
-          float v[4];
+        for (int j = 0; j < kFN; ++j)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v[t] = a[4 * q + t] * rs[i];
-            if constexpr (kBias) v[t] += bv[j][q][t];
-            if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[i][j];
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v[t] = a[4 * q + t] * rs[i];
+              if constexpr (kBias) v[t] += bv[j][q][t];
+              if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
+            }
+            *reinterpret_cast<u32x2*>(stg + (32 * ii + c) * 256 + (((4 * j + q) ^ (c & 15)) << 4) +
+                                      8 * lh) = u32x2{bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3])};
           }
-          *reinterpret_cast<u32x2*>(stg + c * 256 + (((4 * j + q) ^ (c & 15)) << 4) + 8 * lh) =
-              u32x2{bf16_pack(v[0], v[1]), bf16_pack(v[2], v[3])};
-        }
+      }
       // a wave's LDS operations run in order, so the reads below see these
       // writes without a wait; the fence only keeps the compiler's order
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       asm volatile("" ::: "memory");
-      // this pass's 32 x 128 block: rows below e.M - prow0, columns below
-      // e.N - wave_col0 exist
-      const int64_t prow0 = wave_row0 + i * 32;
+      // this pass's (32 kPassTiles) x 128 block: rows below e.M - prow0,
+      // columns below e.N - wave_col0 exist
+      const int64_t prow0 = wave_row0 + pi * 32;
       uint16_t* const ybase = static_cast<uint16_t*>(e.y) + prow0 * e.ldy + wave_col0;
       const int64_t rows_left = e.M - prow0, cols_left = e.N - wave_col0;
       const int k = lane & 15;
-      u32x4 d[8];
+      u32x4 d[8 * kPassTiles];
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 8 * kPassTiles; ++it) {
         const int r = it * 4 + (lane >> 4);
         d[it] = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((k ^ (r & 15)) << 4));
       }
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 8 * kPassTiles; ++it) {
         const int r = it * 4 + (lane >> 4);
         if (r < rows_left && k * 8 < cols_left) {
           uint16_t* yp = ybase + (int64_t)r * e.ldy + k * 8;
