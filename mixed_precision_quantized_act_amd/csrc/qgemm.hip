@@ -19,7 +19,7 @@
 // of 32 x 32 (256 accumulators per lane).  K runs in stages of 32.
 //
 // Data path:
-//   global --(DMA, buffer_load ... lds)--> raw ring in LDS, 4 units of two
+//   global --(DMA, buffer_load ... lds)--> raw ring in LDS, kRawSlots (4) units of two
 //   stages (NVFP4 rows: 32 bytes of codes; INT8 rows: 64 bytes; one 4-byte
 //   word of E4M3 scales per row from a per-tile copy of the scales);
 //   raw ring --(ds_read, expand to fp16 in registers)--> MFMA fragments,
@@ -54,7 +54,12 @@ static constexpr int kThreads = 256;
 static constexpr int kTileM = 256, kTileN = 256;
 static constexpr int kStageK = 32;              // K per stage
 static constexpr int kUnitK = 64;               // K per raw unit (two stages)
-static constexpr int kRawSlots = 4;
+#ifndef QACT_RAW_SLOTS
+#define QACT_RAW_SLOTS 4
+#endif
+// DMA runs kRawSlots - 1 units ahead; 5 slots measured no faster than 4
+static constexpr int kRawSlots = QACT_RAW_SLOTS;
+static_assert(kRawSlots >= 2, "the ring needs a slot being read and one being filled");
 #ifndef QACT_GROUP_M
 #define QACT_GROUP_M 8
 #endif
@@ -300,7 +305,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(bs_base, bd ? (uint32_t)(b_rows * gpr) : st_bytes);
   constexpr uint32_t kOOB = 0x7FFFFFF0u;
 
-  // ---- DMA of raw unit u into slot u % 4.  The destination of one
+  // ---- DMA of raw unit u into slot u % kRawSlots.  The destination of one
   // instruction is 64 consecutive lanes' bytes: 32 NVFP4 rows (lane l: row
   // l/2, LDS half l%2 = global half (l%2) ^ ((row >> 3) & 1)), 16 INT8 rows
   // (lane l: row l/4, LDS chunk l%4 = global chunk (l%4) ^ (((row >> 2) & 1)
@@ -474,10 +479,10 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // (the second stage of a last unit that K ends inside, the reads ahead
   // of the last stage) sees zero words, which expand to zero fragments.
   // Unit v (stages 2v, 2v+1): before the pair, wait for this wave's DMA of
-  // unit v+1 (the two units after it may still be in flight), then a
+  // unit v+1 (the kRawSlots - 2 units after it may still be in flight), then a
   // workgroup barrier, after which that unit is visible to all and the slot
   // of unit v -- whose last words (stage 2v+1) every wave read and waited
-  // for in stage 2v-1 -- takes unit v+4.  Stage t reads the raw words of
+  // for in stage 2v-1 -- takes unit v+kRawSlots.  Stage t reads the raw words of
   // stage t+2 and runs its 32 MFMAs with the expansion of stage t+1's words
   // under them.  The loop body has no branch, so that the accumulators
   // stay in the accumulation registers across it.
@@ -489,7 +494,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   constexpr int kDsReads = QACT_DS_READS > 0 ? QACT_DS_READS : 2 * kFM * kFN;
 #pragma unroll
   for (int u = 0; u < kRawSlots; ++u) issue_unit(u);
-  wait_vm<3 * R::kLoads>();
+  wait_vm<(kRawSlots - 1) * R::kLoads>();
   barrier();
   Ops opA, opB;
   RawS rwA, rwB;
@@ -512,10 +517,10 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     pin_ops(nxt);
   };
   auto sync_unit = [&](int t) {
-    wait_vm<2 * R::kLoads>();
+    wait_vm<(kRawSlots - 2) * R::kLoads>();
     wait_lds();
     barrier();
-    issue_unit((t >> 1) + 4);
+    issue_unit((t >> 1) + kRawSlots);
   };
   for (int t = 0; t < nk; t += 2) {
     sync_unit(t);
