@@ -5,8 +5,11 @@
 //
 // All kernels stream bf16 with 16-byte loads.  NVFP4 runs two passes: a
 // tensor |x| max (per-workgroup partial maxima into scratch) and the
-// encoder, whose workgroups each fold the partial maxima into s_T before
-// encoding four 16-element groups per thread.  INT8 gives each token row
+// encoder.  The encoder gives each lane one 16-byte vector (half a
+// 16-element group) per load, so that a wave's load covers 1 KB of
+// consecutive memory; the two halves of a group sit in neighbouring lanes,
+// which exchange their maxima through one DPP move.  Its first loads are
+// issued before its workgroup folds the partial maxima into s_T.  INT8 gives each token row
 // to one wave: the row stays in registers between the row max (wave
 // shuffles) and the encode, so it is read from memory once.
 #include "qact_device.h"
@@ -17,35 +20,42 @@ namespace qact {
 // ---------------------------------------------------------------- NVFP4 --
 
 static constexpr int kUnroll = 4;
+static constexpr int kPartsMax = 1024;          // partial maxima of the amax pass, at most
 
 __device__ __forceinline__ uint32_t abs_max8(u32x4 a, uint32_t mx) {
   return max(mx, fold_max(abs_max8_pk(a, u16x2{0, 0})));
 }
 
+// Max over the workgroup (at most 16 waves), written by thread 0.
 __device__ __forceinline__ void block_max_to(float v, float* dst) {
-  __shared__ float red[4];
+  __shared__ float red[16];
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  if (threadIdx.x == 0) *dst = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) {
+    float m = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+    *dst = m;
+  }
 }
 
 // Partial tensor amax.  CONTIG (ldx == K): one flat sweep of 16-byte
 // vectors, kUnroll per thread in flight; otherwise row by row.
 template <bool CONTIG>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
                   float* __restrict__ partial) {
   uint32_t mx = 0;
   if (CONTIG) {
     const int64_t nvec = M * K / 8;
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-    for (int64_t v0 = (int64_t)blockIdx.x * 256 * kUnroll + threadIdx.x; v0 < nvec;
-         v0 += (int64_t)gridDim.x * 256 * kUnroll) {
+    const int64_t bs = blockDim.x;
+    for (int64_t v0 = (int64_t)blockIdx.x * bs * kUnroll + threadIdx.x; v0 < nvec;
+         v0 += (int64_t)gridDim.x * bs * kUnroll) {
       u32x4 r[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t v = v0 + u * 256;
+        const int64_t v = v0 + u * bs;
         r[u] = v < nvec ? xv[v] : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
@@ -54,29 +64,61 @@ nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t 
   } else {
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
       const u32x4* xv = reinterpret_cast<const u32x4*>(x + row * ldx);
-      for (int64_t v = threadIdx.x; v < K / 8; v += 256) mx = abs_max8(xv[v], mx);
+      for (int64_t v = threadIdx.x; v < K / 8; v += blockDim.x) mx = abs_max8(xv[v], mx);
     }
   }
   block_max_to(__uint_as_float(mx << 16), partial + blockIdx.x);
 }
 
-// Encoder: G consecutive 16-element groups of one row per thread (G = 4
-// when K % 64 == 0: 128 bytes read, 32 bytes of codes and one 32-bit word
-// of scales written).  s_T from the partial maxima (or *tscale when
-// given); workgroup 0 publishes s_T.
-template <int G>
+// Encoder: vector v (8 bf16 of row v / (K/8), column 8 (v % (K/8))) goes
+// to lane v % 256 of the workgroup's sweep, U vectors per lane in flight;
+// s_T = amax / (6 * 448) unless given, then the steps of the NVFP4 encode
+// per group (6Bit-Diffusion, abstract: one E4M3 scale per 16 elements and
+// one float32 tensor scale).  K % 16 == 0, so a group is the even vector v and v + 1, held
+// by lanes 2j and 2j+1.  Outputs are indexed by v alone: code word v of
+// the [M][K/2] code array and scale byte v / 2 of the [M][K/16] scales.
+template <int U>
 __global__ void __launch_bounds__(256)
-nvfp4_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                    uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-                    float* __restrict__ tscale, const float* __restrict__ partial,
-                    int nparts, int given) {
+nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                        uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                        float* __restrict__ tscale, const float* __restrict__ partial,
+                        int nparts, int given) {
+  const int64_t vpr = K / 8;                               // vectors per row
+  const int64_t nvec = M * vpr;
+  const bool contig = ldx == K;
+  const bool small = nvec <= 0xFFFFFFFFll;
+  const int64_t sweep = (int64_t)gridDim.x * 256 * U;
+  const int64_t start = (int64_t)blockIdx.x * 256 * U + threadIdx.x;
+  auto load = [&](int64_t v0, u32x4 (&w)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 256;
+      int64_t off = v * 8;
+      if (!contig) {
+        const int64_t row = small ? (int64_t)((uint32_t)v / (uint32_t)vpr) : v / vpr;
+        off = row * ldx + (v - row * vpr) * 8;
+      }
+      w[u] = v < nvec ? *reinterpret_cast<const u32x4*>(x + off) : u32x4{0, 0, 0, 0};
+    }
+  };
+  // s_T first -- given, or the tensor max folded from the amax pass's
+  // partial maxima (measured faster than issuing the first loads ahead of
+  // the fold) -- then the sweeps
   __shared__ float red[4];
   float s_t;
   if (given) {
     s_t = *tscale;
   } else {
+    // at most kPartsMax partial maxima: all loads issued at once
+    float pv[kPartsMax / 256];
+#pragma unroll
+    for (int j = 0; j < kPartsMax / 256; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      pv[j] = i < nparts ? partial[i] : 0.0f;
+    }
     float v = 0.0f;
-    for (int i = threadIdx.x; i < nparts; i += blockDim.x) v = fmaxf(v, partial[i]);
+#pragma unroll
+    for (int j = 0; j < kPartsMax / 256; ++j) v = fmaxf(v, pv[j]);
     v = wave_max(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -85,36 +127,23 @@ nvfp4_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = s_t;
   }
   const float g = recip0(6.0f * s_t);
-  const uint32_t cpr = (uint32_t)(K / (16 * G));          // thread chunks per row
-  const uint64_t total = (uint64_t)M * cpr;
-  for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (uint64_t)gridDim.x * blockDim.x) {
-    const uint64_t row = total < 0xFFFFFFFFull ? (uint32_t)t / cpr : t / cpr;
-    const uint32_t c = (uint32_t)(t - row * cpr);
-    const u32x4* p = reinterpret_cast<const u32x4*>(x + row * ldx + (int64_t)c * 16 * G);
-    u32x4 w[2 * G];
+  uint32_t* const q32 = reinterpret_cast<uint32_t*>(q);
+  for (int64_t v0 = start; v0 < nvec; v0 += sweep) {
+    u32x4 w[U];
+    load(v0, w);
 #pragma unroll
-    for (int i = 0; i < 2 * G; ++i) w[i] = p[i];
-    uint32_t sc_word = 0;
-    u32x2 codes[G];
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const uint32_t mx = fold_max(abs_max8_pk(w[2 * gg + 1], abs_max8_pk(w[2 * gg], u16x2{0, 0})));
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 256;
+      const uint32_t own = fold_max(abs_max8_pk(w[u], u16x2{0, 0}));
+      // the partner lane's maximum: quad_perm [1, 0, 3, 2] swaps lanes 2j, 2j+1
+      const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, false);
+      const uint32_t mx = max(own, other);
       const uint32_t enc = e4m3_encode(__uint_as_float(mx << 16) * g);
       const float inv = recip0(e4m3_decode(enc) * s_t);
-      codes[gg] = u32x2{e2m1_pack8(w[2 * gg], inv), e2m1_pack8(w[2 * gg + 1], inv)};
-      sc_word |= enc << (8 * gg);
-    }
-    uint8_t* qp = q + row * (K / 2) + (int64_t)c * 8 * G;
-    if (G == 4) {
-      reinterpret_cast<u32x4*>(qp)[0] = u32x4{codes[0][0], codes[0][1], codes[1][0], codes[1][1]};
-      reinterpret_cast<u32x4*>(qp)[1] = u32x4{codes[2][0], codes[2][1], codes[3][0], codes[3][1]};
-      *reinterpret_cast<uint32_t*>(scales + row * (K / 16) + c * G) = sc_word;
-    } else {
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        reinterpret_cast<u32x2*>(qp)[gg] = codes[gg];
-        scales[row * (K / 16) + c * G + gg] = (uint8_t)(sc_word >> (8 * gg));
+      const uint32_t codes = e2m1_pack8(w[u], inv);
+      if (v < nvec) {
+        q32[v] = codes;
+        if ((v & 1) == 0) scales[v >> 1] = (uint8_t)enc;
       }
     }
   }
@@ -177,6 +206,12 @@ int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t
 // ----------------------------------------------------------------- host --
 
 static constexpr int kAmaxBlocks = 1024;
+static_assert(kAmaxBlocks <= kPartsMax, "encoder folds at most kPartsMax partial maxima");
+// encoder: vectors in flight per lane, and at most this many workgroups
+// (one resident round; measured against 2 vectors per lane and an uncapped
+// grid, which pay the s_T fold again in every later workgroup)
+static constexpr int kEncU = 4;
+static constexpr int kEncBlocks = 2048;
 
 size_t nvfp4_quant_ws_bytes(int64_t, int64_t) { return kAmaxBlocks * sizeof(float); }
 
@@ -198,17 +233,11 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool g4 = K % 64 == 0 && (reinterpret_cast<uintptr_t>(scales) & 3u) == 0;
-  const int64_t chunks = M * (K / (g4 ? 64 : 16));
-  int64_t eblk = (chunks + 255) / 256;
-  if (eblk > 8192) eblk = 8192;
+  int64_t eblk = (M * (K / 8) + 256 * kEncU - 1) / (256 * kEncU);
+  if (eblk > kEncBlocks) eblk = kEncBlocks;
   if (eblk < 1) eblk = 1;
-  if (g4)
-    hipLaunchKernelGGL(nvfp4_encode_kernel<4>, dim3((unsigned)eblk), dim3(256), 0, stream, x, M,
-                       K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0);
-  else
-    hipLaunchKernelGGL(nvfp4_encode_kernel<1>, dim3((unsigned)eblk), dim3(256), 0, stream, x, M,
-                       K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0);
+  hipLaunchKernelGGL(nvfp4_encode_vec_kernel<kEncU>, dim3((unsigned)eblk), dim3(256), 0, stream,
+                     x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0);
   return hipGetLastError();
 }
 

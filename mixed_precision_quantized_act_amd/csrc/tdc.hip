@@ -31,6 +31,7 @@ namespace qact {
 static constexpr int kRedBlocks = QACT_TDC_BLOCKS;
 static constexpr int kThreads = 256;
 static constexpr int kUnroll = QACT_TDC_UNROLL;
+static_assert(kRedBlocks % kThreads == 0, "finalize loads kRedBlocks / kThreads rows per thread");
 
 enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3, MODE_COS = 4 };
 
@@ -152,12 +153,20 @@ tdc_finalize_kernel(const double* __restrict__ partial, int rows, int ncols,
   __shared__ double red[4][kThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int r = threadIdx.x; r < rows; r += kThreads) {
-    const double4 p = reinterpret_cast<const double4*>(partial)[r];
-    s[0] += p.x;
-    s[1] += p.y;
-    s[2] += p.z;
-    s[3] += p.w;
+  // rows <= kRedBlocks: every load issued before the first add
+  constexpr int kPer = kRedBlocks / kThreads;
+  double4 p[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int r = threadIdx.x + kThreads * j;
+    p[j] = r < rows ? reinterpret_cast<const double4*>(partial)[r] : double4{0.0, 0.0, 0.0, 0.0};
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    s[0] += p[j].x;
+    s[1] += p[j].y;
+    s[2] += p[j].z;
+    s[3] += p[j].w;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
