@@ -135,7 +135,7 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
-  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
 int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
@@ -157,7 +157,7 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
   return hip_status(
-      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
 // NVFP4 output of the linear (activation quantization of its consumer,
@@ -198,7 +198,7 @@ int qlinear_nvfp4_q(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {nullptr, N, 0, epi == QA_EPI_GELU_TANH, bias, y_q, y_s, y_ts};
-  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+  return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
 int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
@@ -217,7 +217,7 @@ int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q, cons
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {nullptr, N, 0, epi == QA_EPI_GELU_TANH, bias, y_q, y_s, y_ts};
-  return hip_status(launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, stream));
+  return hip_status(launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
 size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {

@@ -33,15 +33,17 @@ size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                              const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                              int64_t M, int64_t N, int64_t K, const GemmOut& o, void* ws,
-                             hipStream_t stream);
+                             size_t ws_bytes, hipStream_t stream);
 size_t int8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
-// workspace bytes a call actually uses (INT8 reads the weight scales in
-// place when K is a multiple of 64 and w_s is 4-byte aligned)
+// the least workspace a call accepts (INT8 reads the weight scales in
+// place when K is a multiple of 64 and w_s is 4-byte aligned); with the
+// full *_gemm_ws_bytes the last round of tiles is split along K
 size_t nvfp4_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void* w_s);
 size_t int8_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void* w_s);
 hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
                             const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
-                            int64_t K, const GemmOut& o, void* ws, hipStream_t stream);
+                            int64_t K, const GemmOut& o, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 size_t reduce_ws_bytes(int64_t n);

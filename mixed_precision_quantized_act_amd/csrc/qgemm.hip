@@ -182,7 +182,20 @@ struct GemmArgs {
   const float* w_ts;     // weight tensor scale
   const float* a_rs;     // INT8: per-row activation scale
   int b_direct;          // W's scale words read from the [N][K/16] array itself
+  // K split of the last, partly filled round of tiles (see split_plan)
+  int main_tiles;        // tiles computed whole, by workgroups 0 .. grid_main-1
+  int grid_main;         // a multiple of 8
+  int splits;            // K slices per tail tile (1: no split)
+  int split_units;       // raw units per slice (the last slice may have fewer)
+  float* part;           // slice partial sums, kPartTile floats per (tail tile, slice)
 };
+// fp32 partial sums of one tile: 4 waves x 256 accumulators x 64 lanes
+static constexpr int kPartTile = 4 * 256 * 64;
+// K split of the last round of tiles (see split_plan): CUs of the device
+// (one workgroup each) and slices per tile, at most
+static constexpr int kCUs = 256;
+static constexpr int kMaxSplits = 4;
+static constexpr int kSplitMinSaved = 24;   // raw units a split must take off the last round
 
 // Raw buffer (stride 0) over [base, base + bytes): loads at offsets >=
 // bytes return zero.  Both values must be wave-uniform; they are passed
@@ -257,7 +270,15 @@ struct RawWords<true> {
   typedef u32x4 A;       // INT8: the lane's 16 bytes of a row's stage
 };
 
-template <bool I8, int kEpi>
+// Launch modes: kWhole -- whole tiles (all of them, or all but the tail
+// tiles of a K-split call); kSlice -- one K slice of a tail tile per
+// workgroup, storing its fp32 partial sums; kFixup -- one workgroup per tail
+// tile, adding the slices' partial sums (in slice order) and running the
+// epilogue.  Each is its own kernel so that the whole-tile kernel carries
+// none of the slice bookkeeping.
+enum { kWhole = 0, kSlice = 1, kFixup = 2 };
+
+template <bool I8, int kEpi, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 qgemm_kernel(GemmArgs g, EpiArgs e) {
   using R = Raw<I8>;
@@ -267,10 +288,22 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // XCD-aware tile order: hardware deals workgroups to the 8 XCDs in turn;
   // give each XCD a contiguous range of logical tiles, grouped kGroupM
   // tile-rows at a time so that concurrent tiles share A rows and B rows.
-  const int total = g.mt * g.nt;
-  const int per_xcd = (total + 7) / 8;
-  const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (logical >= total) return;
+  // A kSlice workgroup computes slice `slice` of tail tile main_tiles +
+  // bid / splits: raw units u_begin .. u_begin + u_count - 1.
+  const int bid = (int)blockIdx.x;
+  int logical, slice = 0, u_begin = 0, u_count = g.units;
+  if constexpr (kMode == kWhole) {
+    const int per_xcd = (g.main_tiles + 7) / 8;
+    logical = (bid & 7) * per_xcd + (bid >> 3);
+    if (logical >= g.main_tiles) return;
+  } else if constexpr (kMode == kSlice) {
+    logical = g.main_tiles + bid / g.splits;
+    slice = bid % g.splits;
+    u_begin = slice * g.split_units;
+    u_count = min(g.units - u_begin, g.split_units);
+  } else {
+    logical = g.main_tiles + bid;
+  }
   const int group = logical / (kGroupM * g.nt);
   const int first_m = group * kGroupM;
   const int gsz = min(g.mt - first_m, kGroupM);
@@ -286,23 +319,32 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
 
   // Buffer resources based at this tile's first row; rows past the operand
   // fall outside the range and load zero.
+  // A K slice starts its buffers u_begin units in (a_lim, b_lim: the row
+  // bytes left from there).
   const int64_t a_row = I8 ? K : K / 2, b_row = K / 2;
   const int64_t a_rows = min<int64_t>(e.M - m0, kTileM), b_rows = min<int64_t>(e.N - n0, kTileN);
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.a + m0 * a_row, (uint32_t)(a_rows * a_row));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(g.b + n0 * b_row, (uint32_t)(b_rows * b_row));
+  const uint32_t a_skip = (uint32_t)u_begin * (I8 ? 64u : 32u), b_skip = (uint32_t)u_begin * 32u;
+  const uint32_t a_lim = (uint32_t)a_row - a_skip, b_lim = (uint32_t)b_row - b_skip;
+  const __amdgpu_buffer_rsrc_t ra =
+      buffer_rsrc(g.a + m0 * a_row + a_skip, (uint32_t)(a_rows * a_row) - a_skip);
+  const __amdgpu_buffer_rsrc_t rb =
+      buffer_rsrc(g.b + n0 * b_row + b_skip, (uint32_t)(b_rows * b_row) - b_skip);
   // Scale words: word u * 256 + r of the tile's re-laid-out copy holds the
   // 4 scales of row r and unit u; with b_direct (K a multiple of 64, rows
   // are whole words) W's word is bytes 4u .. 4u+3 of row r of its array.
   const uint32_t gpr = (uint32_t)(K / 16);
   const bool bd = g.b_direct != 0;
-  const uint32_t st_bytes = (uint32_t)g.units * 1024u;
+  const uint32_t s_skip = (uint32_t)u_begin * 1024u;
+  const uint32_t st_bytes = (uint32_t)g.units * 1024u - s_skip;
   const uint8_t* const bs_base =
-      bd ? reinterpret_cast<const uint8_t*>(g.b_st) + n0 * gpr
-         : reinterpret_cast<const uint8_t*>(g.b_st + (size_t)tn * g.units * 256);
-  const __amdgpu_buffer_rsrc_t ras =
-      buffer_rsrc(I8 ? static_cast<const void*>(g.b_st) : g.a_st + (size_t)tm * g.units * 256,
-                  I8 ? 0u : st_bytes);
-  const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(bs_base, bd ? (uint32_t)(b_rows * gpr) : st_bytes);
+      bd ? reinterpret_cast<const uint8_t*>(g.b_st) + n0 * gpr + 4 * u_begin
+         : reinterpret_cast<const uint8_t*>(g.b_st + (size_t)tn * g.units * 256) + s_skip;
+  const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(
+      I8 ? static_cast<const void*>(g.b_st)
+         : reinterpret_cast<const uint8_t*>(g.a_st + (size_t)tm * g.units * 256) + s_skip,
+      I8 ? 0u : st_bytes);
+  const __amdgpu_buffer_rsrc_t rbs =
+      buffer_rsrc(bs_base, bd ? (uint32_t)(b_rows * gpr) - 4u * (uint32_t)u_begin : st_bytes);
   constexpr uint32_t kOOB = 0x7FFFFFF0u;
 
   // ---- DMA of raw unit u into slot u % kRawSlots.  The destination of one
@@ -315,7 +357,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // meet a zero scale word.
   auto issue_unit = [&](int u) {
     uint8_t* s = smem + (u % kRawSlots) * R::kSlot;
-    const bool real = u < g.units;                  // past the last unit: zeros into a free slot
+    const bool real = u < u_count;                  // past the last unit: zeros into a free slot
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = wave + 4 * i;
@@ -323,10 +365,8 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       const uint32_t half = (uint32_t)((lane & 1) ^ ((row >> 3) & 1));
       const uint32_t kb = (uint32_t)u * 32u + half * 16u;     // byte in an NVFP4 row
       if constexpr (!I8)
-        dma16(ra, s + R::kA + blk * 1024,
-              real && kb < (uint32_t)b_row ? row * (uint32_t)a_row + kb : kOOB);
-      dma16(rb, s + R::kB + blk * 1024,
-            real && kb < (uint32_t)b_row ? row * (uint32_t)b_row + kb : kOOB);
+        dma16(ra, s + R::kA + blk * 1024, real && kb < b_lim ? row * (uint32_t)a_row + kb : kOOB);
+      dma16(rb, s + R::kB + blk * 1024, real && kb < b_lim ? row * (uint32_t)b_row + kb : kOOB);
     }
     if constexpr (I8) {
 #pragma unroll
@@ -335,7 +375,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
         const uint32_t row = (uint32_t)(16 * blk + (lane >> 2));
         const uint32_t c = (uint32_t)((lane & 3) ^ (((row >> 2) & 1) * 2));
         const uint32_t kb = (uint32_t)u * 64u + c * 16u;
-        dma16(ra, s + R::kA + blk * 1024, real && kb < (uint32_t)K ? row * (uint32_t)a_row + kb : kOOB);
+        dma16(ra, s + R::kA + blk * 1024, real && kb < a_lim ? row * (uint32_t)a_row + kb : kOOB);
       }
     }
     const uint32_t srow = (uint32_t)(64 * wave + lane);
@@ -486,12 +526,13 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // stage t+2 and runs its 32 MFMAs with the expansion of stage t+1's words
   // under them.  The loop body has no branch, so that the accumulators
   // stay in the accumulation registers across it.
-  const int nk = 2 * g.units;
+  const int nk = 2 * u_count;
   // the raw-word reads of stage t+2 (NVFP4: 16, INT8: 12) go one per MFMA
   // from the start of the stage: the scheduling template offers a read
   // slot after every MFMA (measured 12 % faster for NVFP4 and 4 % for INT8
   // than offering 8 slots)
   constexpr int kDsReads = QACT_DS_READS > 0 ? QACT_DS_READS : 2 * kFM * kFN;
+  if constexpr (kMode != kFixup) {
 #pragma unroll
   for (int u = 0; u < kRawSlots; ++u) issue_unit(u);
   wait_vm<(kRawSlots - 1) * R::kLoads>();
@@ -528,14 +569,80 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     compute(t + 1, opB, opA, rwA, rwB);
   }
 
+  wait_vm<0>();          // no DMA into LDS outlives the workgroup
+  __syncthreads();       // every wave is past its last read of the ring
+
+  // ---- K slice of a tail tile: store the partial sums for the fixup
+  // launch and stop.  Partial chunk (i, j, r4) -- accumulators 4 r4 .. 4 r4
+  // + 3 of MFMA tile (i, j) -- of lane l of wave w sits at f32x4 index
+  // (w * 64 + chunk) * 64 + l of the slice's kPartTile floats.
+  if constexpr (kMode == kSlice) {
+    f32x4* const mine = reinterpret_cast<f32x4*>(g.part) +
+                        ((size_t)(logical - g.main_tiles) * g.splits + slice) * (kPartTile / 4) +
+                        wave * 4096 + lane;
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          mine[((i * kFN + j) * 4 + r4) * 64] =
+              f32x4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+    return;
+  }
+  } else {
+    // the tile's sum over its K slices, added in slice order
+    const f32x4* const base = reinterpret_cast<const f32x4*>(g.part) +
+                              (size_t)(logical - g.main_tiles) * g.splits * (kPartTile / 4) +
+                              wave * 4096 + lane;
+    const int ns = g.splits;
+    constexpr int kPair = 2;              // MFMA tiles whose chunks load together
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j0 = 0; j0 < kFN; j0 += kPair) {
+        // the 4 chunks of MFMA tiles (i, j0 .. j0 + kPair - 1) from every
+        // slice, loads issued together
+        f32x4 v[kPair][4][kMaxSplits];
+#pragma unroll
+        for (int jj = 0; jj < kPair; ++jj)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int sl = 0; sl < kMaxSplits; ++sl)
+              v[jj][r4][sl] =
+                  sl < ns ? base[(size_t)sl * (kPartTile / 4) + ((i * kFN + j0 + jj) * 4 + r4) * 64]
+                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int jj = 0; jj < kPair; ++jj) {
+          f32x16 tot;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 sum = v[jj][r4][0];
+#pragma unroll
+            for (int sl = 1; sl < kMaxSplits; ++sl)
+              if (sl < ns) sum += v[jj][r4][sl];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tot[4 * r4 + t] = sum[t];
+          }
+          // into the accumulation registers through an MFMA with zero
+          // operands (it adds +0, which changes no sum: none is -0), so
+          // that the 256 sums do not crowd the ordinary registers
+          const f16x8 z = {};
+          acc[i][j0 + jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, tot, 0, 0, 0);
+        }
+        // bound the loads in flight to kPair MFMA tiles' chunks
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  if constexpr (kMode != kSlice) {
+
   // ---- epilogue.  Lane (h, c) of accumulator tile (i, j) owns row 32i + c
   // and, for q = 0..3, the 4 consecutive columns 32j + 8q + 4h .. +3
   // (h = lane/32, c = lane%32).  Scale, bias, GELU and the rounding are
   // applied in registers; row scales and bias are read once per tile, rows
   // and columns past the output reading the last valid entry (they are
   // never stored).
-  wait_vm<0>();          // no DMA into LDS outlives the workgroup
-  __syncthreads();       // every wave is past its last read of the ring
   const int64_t wave_row0 = m0 + wm * 128;
   const int64_t wave_col0 = n0 + wn * 128;
   const int c = lane & 31;
@@ -736,6 +843,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     else
       store(F(), F());
   }
+  }
 }
 
 // ---------------------------------------------------------------- host --
@@ -747,12 +855,52 @@ static int vec_ok(const GemmOut& o) {
 static size_t scale_tiles_bytes(int64_t rows, int64_t K) {
   return (size_t)((rows + kTileM - 1) / kTileM) * (size_t)units_of(K) * 1024u;
 }
+static size_t r256(size_t v) { return (v + 255) / 256 * 256; }
 
-size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  return (size_t)round_up((int64_t)scale_tiles_bytes(M, K), 256) + scale_tiles_bytes(N, K);
+// K split of the last round.  With one workgroup per CU the tiles run in
+// rounds of kCUs; when the last round is at most half full, each of its
+// `tail` tiles is split along K into `splits` slices (at most kMaxSplits,
+// at least 2 raw units each) so that the round holds tail * splits
+// workgroups of 1/splits the length.  A pure function of the shape, so
+// that workspace sizes are too; on a device with another CU count the plan
+// is only less well fitted.  Every slice stores its fp32 partial sums in the workspace;
+// a second launch adds them per tail tile and runs the epilogue (no
+// workgroup waits for another inside a launch).
+struct SplitPlan {
+  int main_tiles, tail, splits, split_units;
+};
+static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  const int units = (int)units_of(K);
+  const int total = (int)(((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN));
+  SplitPlan p = {total, 0, 1, units};
+  const int tail = total % kCUs;
+  if (tail == 0 || 2 * tail > kCUs) return p;
+  const int s = min(min(kCUs / tail, kMaxSplits), units / 2);
+  // worth it only if the round gets shorter by more than the slice and
+  // fixup launches cost: measured, the fixup alone takes about as long as
+  // 15-20 raw units of a tile (the QKV shape, 30 units in 3 slices, ran
+  // 5 % slower split; the 7680-wide down projection, 120 units in 4, 10 %
+  // faster)
+  if (s < 2 || units * (s - 1) / s < kSplitMinSaved) return p;
+  p.main_tiles = total - tail;
+  p.tail = tail;
+  p.split_units = (units + s - 1) / s;
+  p.splits = (units + p.split_units - 1) / p.split_units;   // no empty slice
+  return p;
+}
+// the slices' partial sums
+static size_t split_ws_bytes(const SplitPlan& p) {
+  return (size_t)p.tail * p.splits * kPartTile * 4;
 }
 
-size_t int8_gemm_ws_bytes(int64_t, int64_t N, int64_t K) { return scale_tiles_bytes(N, K); }
+size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return r256(scale_tiles_bytes(M, K)) + r256(scale_tiles_bytes(N, K)) +
+         split_ws_bytes(split_plan(M, N, K));
+}
+
+size_t int8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return r256(scale_tiles_bytes(N, K)) + split_ws_bytes(split_plan(M, N, K));
+}
 
 // INT8: the weight scales are read in place when K is a multiple of 64 and
 // the array is 4-byte aligned (no re-layout launch).  The NVFP4 kernel,
@@ -766,12 +914,14 @@ static bool w_scales_direct(int64_t K, const void* w_s) {
   return QACT_INT8_W_DIRECT && K % kUnitK == 0 && (reinterpret_cast<uintptr_t>(w_s) & 3) == 0;
 }
 
+// the least workspace a call accepts: without the K split (which is used
+// only when the workspace holds nvfp4/int8_gemm_ws_bytes)
 size_t nvfp4_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void*) {
-  return nvfp4_gemm_ws_bytes(M, N, K);
+  return r256(scale_tiles_bytes(M, K)) + scale_tiles_bytes(N, K);
 }
 
-size_t int8_gemm_ws_need(int64_t M, int64_t N, int64_t K, const void* w_s) {
-  return w_scales_direct(K, w_s) ? 0 : int8_gemm_ws_bytes(M, N, K);
+size_t int8_gemm_ws_need(int64_t, int64_t N, int64_t K, const void* w_s) {
+  return w_scales_direct(K, w_s) ? 0 : scale_tiles_bytes(N, K);
 }
 
 static hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
@@ -792,20 +942,33 @@ static hipError_t launch_scale_tiles(const uint8_t* s0, int64_t rows0, uint32_t*
   return hipGetLastError();
 }
 
-template <bool I8, int kEpi>
-static void launch_one(int grid, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
-  if (g_ev_before || g_ev_after)
-    // the events take the dispatch's own start and end timestamps: no
-    // marker packets are added to the stream around the kernel
-    hipExtLaunchKernelGGL((qgemm_kernel<I8, kEpi>), dim3(grid), dim3(kThreads), 0, st,
-                          g_ev_before, g_ev_after, 0u, g, e);
+// The GEMM: the whole tiles, then with a K split the slices of the tail
+// tiles and their fixup.  The events take the dispatches' own start and
+// end timestamps (the start of the first, the end of the last): no marker
+// packets are added to the stream around the kernels.
+template <bool I8, int kEpi, int kMode>
+static void launch_mode(int grid, hipEvent_t before, hipEvent_t after, const GemmArgs& g,
+                        const EpiArgs& e, hipStream_t st) {
+  if (before || after)
+    hipExtLaunchKernelGGL((qgemm_kernel<I8, kEpi, kMode>), dim3(grid), dim3(kThreads), 0, st,
+                          before, after, 0u, g, e);
   else
-    hipLaunchKernelGGL((qgemm_kernel<I8, kEpi>), dim3(grid), dim3(kThreads), 0, st, g, e);
+    hipLaunchKernelGGL((qgemm_kernel<I8, kEpi, kMode>), dim3(grid), dim3(kThreads), 0, st, g, e);
+}
+
+template <bool I8, int kEpi>
+static void launch_one(int, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
+  const int tail = g.mt * g.nt - g.main_tiles;
+  if (g.main_tiles)
+    launch_mode<I8, kEpi, kWhole>(g.grid_main, g_ev_before, tail ? nullptr : g_ev_after, g, e, st);
+  if (!tail) return;
+  launch_mode<I8, kEpiPlain, kSlice>(tail * g.splits, g.main_tiles ? nullptr : g_ev_before,
+                                     nullptr, g, e, st);
+  launch_mode<I8, kEpi, kFixup>(tail, nullptr, g_ev_after, g, e, st);
 }
 
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st) {
-  const int total = g.mt * g.nt;
-  const int grid = 8 * ((total + 7) / 8);
+  const int grid = g.grid_main;
   int kind = kEpiGeneral;
   if (e.yq)
     kind = kEpiQuant;
@@ -830,25 +993,33 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
   return hipGetLastError();
 }
 
-static GemmArgs base_args(int64_t M, int64_t N, int64_t K) {
+// split: the workspace region of the K split (null: no split)
+static GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint8_t* split) {
   GemmArgs g = {};
   g.K = K;
   g.units = (int)units_of(K);
   g.nk = (int)((K + kStageK - 1) / kStageK);
   g.mt = (int)((M + kTileM - 1) / kTileM);
   g.nt = (int)((N + kTileN - 1) / kTileN);
+  const SplitPlan p = split ? split_plan(M, N, K) : SplitPlan{g.mt * g.nt, 0, 1, g.units};
+  g.main_tiles = p.main_tiles;
+  g.grid_main = 8 * ((p.main_tiles + 7) / 8);
+  g.splits = p.splits;
+  g.split_units = p.split_units;
+  if (p.tail) g.part = reinterpret_cast<float*>(split);
   return g;
 }
 
 hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                              const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                              int64_t M, int64_t N, int64_t K, const GemmOut& o, void* ws,
-                             hipStream_t st) {
+                             size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  GemmArgs g = base_args(M, N, K);
+  uint8_t* const w8 = static_cast<uint8_t*>(ws);
+  const size_t tiles = r256(scale_tiles_bytes(M, K)) + r256(scale_tiles_bytes(N, K));
+  GemmArgs g = base_args(M, N, K, ws_bytes >= nvfp4_gemm_ws_bytes(M, N, K) ? w8 + tiles : nullptr);
   uint32_t* a_st = static_cast<uint32_t*>(ws);
-  uint32_t* b_st = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
-                                               round_up((int64_t)scale_tiles_bytes(M, K), 256));
+  uint32_t* b_st = reinterpret_cast<uint32_t*>(w8 + r256(scale_tiles_bytes(M, K)));
   hipError_t err = launch_scale_tiles(a_s, M, a_st, w_s, N, b_st, K, st);
   if (err != hipSuccess) return err;
   g.b_direct = 0;
@@ -864,9 +1035,13 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
 
 hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
                             const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
-                            int64_t K, const GemmOut& o, void* ws, hipStream_t st) {
+                            int64_t K, const GemmOut& o, void* ws, size_t ws_bytes,
+                            hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  GemmArgs g = base_args(M, N, K);
+  uint8_t* const w8 = static_cast<uint8_t*>(ws);
+  GemmArgs g = base_args(M, N, K,
+                         ws_bytes >= int8_gemm_ws_bytes(M, N, K) ? w8 + r256(scale_tiles_bytes(N, K))
+                                                                 : nullptr);
   g.b_direct = w_scales_direct(K, w_s);
   if (g.b_direct) {
     g.b_st = reinterpret_cast<const uint32_t*>(w_s);

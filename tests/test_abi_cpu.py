@@ -79,8 +79,23 @@ def test_qlinear_validation():
     # rows rounded up to tiles of 256
     units = (1920 + 63) // 64
     tiles = lambda r: (r + 255) // 256
-    assert qa.qlinear_workspace(qa.NVFP4, 17776, 5760, 1920) >= (tiles(17776) + tiles(5760)) * units * 1024
-    assert qa.qlinear_workspace(qa.INT8, 17776, 5760, 1920) == tiles(5760) * units * 1024
+    r256 = lambda b: (b + 255) // 256 * 256
+    # K split of the last round of tiles: 70 x 23 = 1610 tiles are 6 rounds
+    # of 256 and 74 more; 3 slices of 10 units would take only 20 units off
+    # the last round (less than the 24 a split must save), so no split
+    assert qa.qlinear_workspace(qa.NVFP4, 17776, 5760, 1920) == \
+        r256(tiles(17776) * units * 1024) + r256(tiles(5760) * units * 1024)
+    assert qa.qlinear_workspace(qa.INT8, 17776, 5760, 1920) == r256(tiles(5760) * units * 1024)
+    # the down projection: 70 x 8 = 560 = 2 x 256 + 48 tiles, K = 7680 (120
+    # units) in 4 slices of 30 (256 // 48 = 5, at most 4): 90 units saved;
+    # 256 x 256 fp32 partial sums per slice
+    k4 = (7680 + 63) // 64
+    assert qa.qlinear_workspace(qa.INT8, 17776, 1920, 7680) == \
+        r256(8 * k4 * 1024) + 48 * 4 * 256 * 256 * 4
+    # a full last round (8 x 32 = 256 tiles) or one more than half full
+    # (13 x 30 = 390 = 256 + 134) is not split
+    assert qa.qlinear_workspace(qa.INT8, 2048, 8192, 7680) == r256(32 * k4 * 1024)
+    assert qa.qlinear_workspace(qa.INT8, 3328, 7680, 7680) == r256(30 * k4 * 1024)
 
 
 def test_tdc_validation():

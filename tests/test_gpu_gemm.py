@@ -117,6 +117,81 @@ def test_f32_output_elementwise_bound(M, N, K, path):
     assert np.all(err <= bound), float(np.max(err / bound))
 
 
+def _run_ws(path, a, wq, M, N, K, split, bias=None, gelu=False):
+    """float32 output with the full workspace (the last round of tiles split
+    along K) or one byte short of it (every tile whole)."""
+    qa, t = _qa(), torch()
+    fmt = qa.NVFP4 if path == "nvfp4" else qa.INT8
+    full = qa.qlinear_workspace(fmt, M, N, K)
+    ws = qa.workspace(full)
+    if not split:
+        ws = ws[:full - 1]
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    b = None if bias is None else dev(bias)
+    epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+    w3 = (dev(wq[0]), dev(wq[1]), dev(np.array([wq[2]], np.float32)))
+    if path == "nvfp4":
+        qa.qlinear_nvfp4(dev(a[0]), dev(a[1]), dev(np.array([a[2]], np.float32)), *w3, y, M, N, K,
+                         bias=b, out=qa.OUT_F32, epi=epi, ws=ws)
+    else:
+        qa.qlinear_int8(dev(a[0]), dev(a[1]), *w3, y, M, N, K, bias=b, out=qa.OUT_F32, epi=epi,
+                        ws=ws)
+    t.cuda.synchronize()
+    return host(y).astype(np.float64)
+
+
+# (M, N, K): 9 tiles in 4 slices of 15 units; 6 tiles in 4 slices of 13,
+# 13, 13 and 10 units with K ending inside the last unit; 272 tiles = one
+# whole round of 256 and 16 split in 4 slices of 10; 128 tiles of the
+# down projection's width and depth in 2 slices of 60
+SPLIT_SHAPES = [(600, 700, 3840), (257, 513, 3088), (4352, 4096, 2560), (4096, 1920, 7680)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+def test_k_split_tail_tiles(M, N, K, path):
+    # the K-split tiles agree with whole tiles to the float32 accumulation
+    # bound, and both with the oracle (sampled rows at the large shapes)
+    x, w = _case(M, N, K, seed=19)
+    wq = Q.nvfp4_encode(w)
+    wd = Q.nvfp4_decode(*wq)
+    a = Q.nvfp4_encode(x) if path == "nvfp4" else Q.int8_encode(x)
+    ys = _run_ws(path, a, wq, M, N, K, split=True)
+    yw = _run_ws(path, a, wq, M, N, K, split=False)
+    rows = sample_rows(M, 256, seed=5) if M > 1024 else np.arange(M)
+    if path == "nvfp4":
+        ad = Q.nvfp4_decode(a[0][rows], a[1][rows], a[2])
+    else:
+        ad = Q.int8_decode(a[0][rows], a[1][rows])
+    ref = G.linear_ref(ad, wd)
+    bound = _elementwise_bound(ad, wd, K)
+    for y in (ys, yw):
+        assert np.all(np.abs(y[rows] - ref) <= bound), float(np.max(np.abs(y[rows] - ref) / bound))
+    # whole against split over every output (a wrong or missing slice would
+    # be off by a whole partial sum, a relative error near 1/slices)
+    assert rel_fro(ys, yw) <= 1e-5
+
+
+def test_k_split_exact_sums_bias_gelu():
+    # small integer operands: every partial and every slice sum is exact in
+    # float32, so split and whole tiles give the same bits (bias and GELU
+    # applied once, by the slice that finishes last)
+    # (unit weight scales and power-of-two tensor and row scales: every
+    # partial sum is a multiple of 1/2 below 2^23)
+    M, N, K = 600, 700, 3840
+    rng = np.random.default_rng(23)
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    s = np.float32(2.0) ** rng.integers(-4, 4, M).astype(np.float32)
+    wq = (rng.integers(0, 256, (N, K // 2), dtype=np.uint8),
+          np.full((N, K // 16), 0x38, np.uint8), np.float32(0.125))
+    ref = G.linear_ref(Q.int8_decode(q, s), Q.nvfp4_decode(*wq))
+    np.testing.assert_array_equal(_run_ws("int8", (q, s), wq, M, N, K, split=True), ref)
+    bias = F.f64_to_bf16_rne(rng.normal(0, 0.5, N))
+    ys = _run_ws("int8", (q, s), wq, M, N, K, split=True, bias=bias, gelu=True)
+    yw = _run_ws("int8", (q, s), wq, M, N, K, split=False, bias=bias, gelu=True)
+    np.testing.assert_array_equal(ys, yw)
+
+
 @pytest.mark.parametrize("path", ["nvfp4", "int8"])
 def test_bias_and_gelu(path):
     M, N, K = 200, 300, 256
