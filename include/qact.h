@@ -133,11 +133,17 @@ int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
  * over K -- about K 2^-24 times sum_k |a_k w_k| at worst -- plus the final
  * rounding to the output type; the relative Frobenius error is far below
  * 1e-3.
- * Workspace: qlinear_workspace() bytes (a per-tile copy of the E4M3 scales
- * of the operands, about (M + N) K / 16 bytes), device memory that the
- * call may overwrite.  When K is a multiple of 64 and w_s is 4-byte
- * aligned the INT8 call reads the weight scales in place and uses no
- * workspace (it may then be NULL).
+ * Workspace: qlinear_workspace() bytes, device memory that the call may
+ * overwrite: a per-tile copy of the E4M3 scales of the operands (about
+ * (M + N) K / 16 bytes) and, for shapes whose last round of 256 x 256
+ * tiles (one per CU, 256 CUs) is at most half full and deep enough in K,
+ * fp32 partial sums of that round's tiles split along K into up to 4
+ * slices (256 KB per slice).  A call given less than qlinear_workspace()
+ * but at least the scale copies computes the same outputs without the
+ * split (summed in another order: equal within the accuracy above).  When
+ * K is a multiple of 64 and w_s is 4-byte aligned the INT8 call reads the
+ * weight scales in place and needs no more workspace than the split's (it
+ * may then be NULL, and runs unsplit).
  * y must not overlap any input.  Requires 0 < K, K % 16 == 0, M, N >= 0.
  * ------------------------------------------------------------------------ */
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
