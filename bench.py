@@ -112,14 +112,67 @@ def cpu_baseline(x, w, x_out, delta_prev, rows):
                       f"1 thread, float64 BLAS on {cores} threads; host has {os.cpu_count()} CPUs"}
 
 
+def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
+    """Per-layer qlinear speed of one block's four linears (QKV H->3H, O
+    H->H, up H->F with GELU, down F->H) on M tokens, both activation
+    formats: the GEMM call alone (operands quantized beforehand), median of
+    `reps` event-timed calls."""
+    shapes = {"qkv": (3 * H, H, False), "o": (H, H, False), "up_gelu": (F_, H, True),
+              "down": (H, F_, False)}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    out = {}
+    for name, (N, K, gelu) in shapes.items():
+        w = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        wq, ws_, wts = qa.empty_nvfp4(N, K, dev)
+        qa.act_quant(qa.NVFP4, w.view(torch.int16), wq, ws_, wts, 0,
+                     qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K), dev), stream=stream)
+        x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        aq, asc, ats = qa.empty_nvfp4(M, K, dev)
+        qa.act_quant(qa.NVFP4, x, aq, asc, ats, 0,
+                     qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K), dev), stream=stream)
+        a8, s8 = qa.empty_int8_act(M, K, dev)
+        qa.act_quant(qa.INT8, x, a8, s8, stream=stream)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+        g4 = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, N, K), dev)
+        g8 = qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K), dev)
+        calls = {
+            "nvfp4": lambda: qa.qlinear_nvfp4(aq, asc, ats, wq, ws_, wts, y, M, N, K, epi=epi,
+                                              ws=g4, stream=stream),
+            "int8": lambda: qa.qlinear_int8(a8, s8, wq, ws_, wts, y, M, N, K, epi=epi, ws=g8,
+                                            stream=stream)}
+        rec = {"N": N, "K": K}
+        for fmt, fn in calls.items():
+            fn()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = float(np.median(ts))
+            tfs = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            rec[fmt] = {"us": round(us, 1), "TFLOP/s": round(tfs, 1),
+                        "frac_fp16_peak": round(tfs / PEAK["bf16_TFLOPs"], 4)}
+        out[name] = rec
+        del w, x, y, aq, asc, a8, g4, g8
+    return out
+
+
 def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, steps=10,
-                  delta=0.05):
+                  delta=0.05, cfg=4, modes=("w4a8", "w4a4", "dmpq", "full", "median", "cos")):
     """The CogVideoX-2B-shaped stack (30 blocks; per block the four internal
     linears QKV H->3H, O H->H, up H->F with GELU, down F->H; attention
     replaced by its value slice, no token mixing) over `steps` drifting
     timesteps, entirely through the library, in four modes: uniform W4A8,
     uniform W4A4, DMPQ (masks from the previous step's Gamma, tau set once
-    so that half of the linears are INT8) and DMPQ + TDC.  Returns
+    so that half of the linears are INT8) and DMPQ + TDC ("median": TDC
+    with delta at the DMPQ run's median d; "cos": the cosine rule at the
+    median cosine); other shapes (the 5B-shaped stack: 42 blocks, H 3072,
+    FFN 12288) through L, H, F_ and the synthetic config id `cfg`.  Returns
     ms/step (mean of steps 2..), the INT8 share and the skipped blocks."""
     import math
     import synth
@@ -172,9 +225,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
 
     # the drifting stack inputs x_t = bf16(x_{t-1} + 0.02 N(0,1)), made once
     xs = []
-    x = synth.activations(4, M, H, "normal")
+    x = synth.activations(cfg, M, H, "normal")
     for t in range(steps):
-        x = synth.drift(4, t, x)
+        x = synth.drift(cfg, t, x)
         xs.append(torch.from_numpy(x.view(np.int16).copy()).to(dev).view(bf))
 
     csums = torch.zeros((L, 3), dtype=torch.float64, device=dev)
@@ -260,20 +313,23 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                 "d_median": round(float(np.median(d_seen)), 4) if d_seen else None,
                 "cos_median": round(float(np.median(cos_seen)), 4) if cos_seen else None}
 
-    res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full")}
+    res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full") if m in modes}
     # the synthetic trajectory's block updates change by d ~ d_median from
     # step to step; a threshold at that median shows the skip path's speed
-    if res["dmpq"]["d_median"]:
+    if "median" in modes and res["dmpq"]["d_median"]:
         res["full_delta_at_median_d"] = run("full", delta=res["dmpq"]["d_median"])
     # the cosine rule of Fig. 4 (a variant): threshold at the median cosine
     # of the DMPQ run's successive Deltas (an untimed probe run)
-    probe = run("dmpq", cos_probe=True)
-    if probe["cos_median"] is not None:
-        res["full_cos_at_median"] = run("full", delta=probe["cos_median"], cos_rule=True)
+    if "cos" in modes:
+        probe = run("dmpq", cos_probe=True)
+        if probe["cos_median"] is not None:
+            res["full_cos_at_median"] = run("full", delta=probe["cos_median"], cos_rule=True)
     res["config"] = {"blocks": L, "hidden": H, "ffn": F_, "tokens": M, "steps": steps,
                      "delta": delta, "alpha": 1.0, "beta": 0.01,
                      "block": "QKV -> value slice -> O (+res) -> up+GELU -> down (+res); "
                               "no attention mixing"}
+    res["config"]["linear_TFLOP_per_step_no_skips"] = round(
+        L * 2.0 * M * (3 * H * H + H * H + 2 * F_ * H) / 1e12, 2)
     res["full_vs_dmpq_speedup"] = round(res["dmpq"]["ms_per_step"] / res["full"]["ms_per_step"], 3)
     if "full_delta_at_median_d" in res:
         res["full_at_median_d_vs_dmpq_speedup"] = round(
@@ -292,6 +348,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--stack-steps", type=int, default=10,
                     help="timesteps of the 30-block stack section (0 skips it)")
+    ap.add_argument("--stack5-steps", type=int, default=10,
+                    help="timesteps of the 42-block 5B-shaped stack section (0 skips it)")
     ap.add_argument("--cold-reps", type=int, default=9,
                     help="reps of each bandwidth kernel timed after a 1 GiB cache-evicting read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,6 +578,12 @@ def main():
     del h, hq, hs
     stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
              if args.stack_steps > 0 else None)
+    layers2b = layer_rates(qa, torch, np, dev, stream, M, 1920, 7680)
+    stack5 = None
+    if args.stack5_steps > 0:
+        stack5 = stack_section(qa, torch, np, dev, stream, L=42, H=3072, F_=12288, M=M,
+                               steps=args.stack5_steps, cfg=5, modes=("dmpq", "full", "median"))
+        stack5["per_layer_qlinear"] = layer_rates(qa, torch, np, dev, stream, M, 3072, 12288)
 
     ms_step = wall * 1e3 / args.steps
     flops_step = 2 * 2.0 * M * N * K
@@ -577,6 +641,8 @@ def main():
         "cold": cold,
         "ffn_up_fused_nvfp4_output": ffn_fused,
         "stack_cogvideox2b_shape": stack,
+        "per_layer_qlinear_cogvideox2b_shape": layers2b,
+        "stack_cogvideox5b_shape": stack5,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
