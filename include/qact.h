@@ -257,6 +257,49 @@ int tdc_decide(int t, const double* d_prev, const uint8_t* computed_prev, int L,
  * cos_prev[l] the cosine of the block's last two Deltas (delta_cosine). */
 int tdc_decide_cos(int t, const double* cos_prev, const uint8_t* computed_prev, int L,
                    double threshold, uint8_t* skip);
+/* ---- Device-side step control (a timestep without host decisions) -------
+ * The host loop of a diffusion step decides on the host: DMPQ masks from
+ * Gamma_{t-1} (dmpq_mask) and TDC skips (tdc_decide), after copying the
+ * sums of the previous step back.  These two calls let the whole step be
+ * enqueued -- or captured once in a graph and replayed -- with the
+ * decisions made on the device:
+ *
+ * qa_decide_step: one launch, at the start of step t, on `stream`.  Per
+ * block l (L blocks of J linears), from sums [L][4] as the previous step's
+ * calls left them (S1, S2 of tdc_update for a computed block, of tdc_apply
+ * for a skipped one; S3, S4 of tdc_update), with device state that the
+ * caller zero-fills once before step 0 and that the call carries on:
+ *   t_ctr   int32: steps decided so far (t);
+ *   bstate  u8 [L][4]: the block ran at t-1, Deltas stored (0..2), ring slot
+ *           `last` holding the newest Delta, unused;
+ *   d_prev  f64 [L]: relative L2 distance of the last two Deltas.
+ * It first applies step t-1's outcome as the host loop does (Gamma =
+ * S1/S2; a computed block's Delta went to slot last ^ 1, and d = sqrt(S3) /
+ * sqrt(S4) once two are stored; x/0 = +inf, 0/0 = 0), then decides exactly
+ * as dmpq_mask (alpha, beta: device f32 [L*J]; tau) and tdc_decide (delta)
+ * would on those values, and writes the gate bytes of step t:
+ *   lin_flags u8 [L*J]: 1 = NVFP4 path, 2 = INT8 path, 0 = block skipped;
+ *   blk_flags u8 [L]:   1 / 2 = compute, Delta ring slot last = 0 / 1
+ *                       (tdc_update reads slot last, writes last ^ 1);
+ *                       4 / 8 = skip, tdc_apply with slot last = 0 / 1;
+ *   mask_out [L*J], skip_out [L] (nullable): the decisions themselves.
+ * The ring slots must hold zeros before step 0 (a first Delta is then
+ * compared with zeros: d = +inf, as with no previous Delta).
+ *
+ * qa_set_gate: until cleared (flags NULL), every kernel of every library
+ * call made from the calling thread reads the device byte *flags and does
+ * nothing unless (*flags & bits) != 0 -- the call's outputs, sums
+ * included, are then left as they were.  Host-side checks still run.  A
+ * step thus enqueues every path (both formats of each linear, the compute
+ * and skip paths of each block, the Delta update for either ring slot),
+ * each under its gate byte and bits.  Per thread; bits != 0 when flags is
+ * set. */
+int qa_decide_step(const double* sums, const float* alpha, const float* beta, double tau,
+                   double delta, int L, int J, int* t_ctr, uint8_t* bstate, double* d_prev,
+                   uint8_t* blk_flags, uint8_t* lin_flags, uint8_t* mask_out, uint8_t* skip_out,
+                   hipStream_t stream);
+int qa_set_gate(const uint8_t* flags, uint32_t bits);
+
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
  * inside qlinear) launches its main GEMM kernel with hipExtLaunchKernel so
  * that `before` and `after` take that dispatch's start and end timestamps

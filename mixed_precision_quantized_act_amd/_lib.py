@@ -58,6 +58,9 @@ _SIGS = {
     "dmpq_mask": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_double, _P]),
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
     "qa_set_gemm_events": (ctypes.c_int, [_P, _P]),
+    "qa_set_gate": (ctypes.c_int, [_P, ctypes.c_uint32]),
+    "qa_decide_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                      ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qa_gamma_from_sums": (ctypes.c_double, [_P]),
     "qa_rel_l2_from_sums": (ctypes.c_double, [_P]),
     "qa_rel_err_from_sums": (ctypes.c_double, [_P]),
@@ -326,3 +329,39 @@ def rel_l2_from_sums(sums4):
     if s.size < 4:
         raise ValueError("rel_l2_from_sums: needs the four sums")
     return lib().qa_rel_l2_from_sums(s.ctypes.data)
+
+
+# ------------------------------------------------- device-side step control --
+
+# gate bits of qa_decide_step's flag bytes
+ROUTE_NVFP4, ROUTE_INT8 = 1, 2
+BLK_RUN0, BLK_RUN1, BLK_SKIP0, BLK_SKIP1 = 1, 2, 4, 8
+
+
+def set_gate(flags, bits=0):
+    """Gate every following call of this thread on the device byte `flags`
+    (a uint8 tensor of one element, or a one-element slice): its kernels run
+    only if (flags & bits) != 0.  set_gate(None) clears."""
+    _check("qa_set_gate", lib().qa_set_gate(_ptr(flags), bits if flags is not None else 0))
+
+
+class gate:
+    """Context manager form of set_gate."""
+
+    def __init__(self, flags, bits):
+        self.flags, self.bits = flags, bits
+
+    def __enter__(self):
+        set_gate(self.flags, self.bits)
+
+    def __exit__(self, *exc):
+        set_gate(None)
+
+
+def decide_step(sums, alpha, beta, tau, delta, L, J, t_ctr, bstate, d_prev, blk_flags, lin_flags,
+                mask_out=None, skip_out=None, stream=None):
+    """One timestep's DMPQ masks and TDC skips on the device (qa_decide_step)."""
+    _check("qa_decide_step", lib().qa_decide_step(
+        _ptr(sums), _ptr(alpha), _ptr(beta), tau, delta, L, J, _ptr(t_ctr), _ptr(bstate),
+        _ptr(d_prev), _ptr(blk_flags), _ptr(lin_flags), _ptr(mask_out), _ptr(skip_out),
+        _stream(stream)))

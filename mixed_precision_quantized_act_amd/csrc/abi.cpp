@@ -41,7 +41,14 @@ int check_out(qa_out out, qa_epi epi) {
   return QA_OK;
 }
 
+// the calling thread's gate (qa_set_gate), applied to every launch it makes
+thread_local Gate g_gate = {nullptr, 0u};
+
 }  // namespace
+
+namespace qact {
+Gate current_gate() { return g_gate; }
+}  // namespace qact
 
 extern "C" {
 
@@ -336,6 +343,29 @@ int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
 static double ratio0(double num, double den) {
   if (den == 0.0) return num == 0.0 ? 0.0 : INFINITY;
   return num / den;
+}
+
+// ------------------------------------------------ device-side step control --
+
+int qa_set_gate(const uint8_t* flags, uint32_t bits) {
+  if (flags && bits == 0) return QA_EINVAL;
+  g_gate = Gate{flags, flags ? bits : 0u};
+  return QA_OK;
+}
+
+int qa_decide_step(const double* sums, const float* alpha, const float* beta, double tau,
+                   double delta, int L, int J, int* t_ctr, uint8_t* bstate, double* d_prev,
+                   uint8_t* blk_flags, uint8_t* lin_flags, uint8_t* mask_out, uint8_t* skip_out,
+                   hipStream_t stream) {
+  if (L <= 0 || J <= 0 || L * J > (1 << 24)) return QA_ESHAPE;
+  if (!sums || !alpha || !beta || !t_ctr || !bstate || !d_prev || !blk_flags || !lin_flags)
+    return QA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(sums) & 7u) || (reinterpret_cast<uintptr_t>(d_prev) & 7u) ||
+      (reinterpret_cast<uintptr_t>(alpha) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u) ||
+      (reinterpret_cast<uintptr_t>(t_ctr) & 3u) || (reinterpret_cast<uintptr_t>(bstate) & 3u))
+    return QA_EALIGN;
+  return hip_status(launch_decide(sums, alpha, beta, tau, delta, L, J, t_ctr, bstate, d_prev,
+                                  blk_flags, lin_flags, mask_out, skip_out, stream));
 }
 
 double qa_gamma_from_sums(const double* sums2) {

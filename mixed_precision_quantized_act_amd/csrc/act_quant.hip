@@ -42,9 +42,10 @@ __device__ __forceinline__ void block_max_to(float v, float* dst) {
 // Partial tensor amax.  CONTIG (ldx == K): one flat sweep of 16-byte
 // vectors, kUnroll per thread in flight; otherwise row by row.
 template <bool CONTIG>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(256)
 nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                  float* __restrict__ partial) {
+                  float* __restrict__ partial, Gate gate) {
+  if (gated_off(gate)) return;
   uint32_t mx = 0;
   if (CONTIG) {
     const int64_t nvec = M * K / 8;
@@ -82,7 +83,8 @@ __global__ void __launch_bounds__(256)
 nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
                         uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                         float* __restrict__ tscale, const float* __restrict__ partial,
-                        int nparts, int given) {
+                        int nparts, int given, Gate gate) {
+  if (gated_off(gate)) return;
   const int64_t vpr = K / 8;                               // vectors per row
   const int64_t nvec = M * vpr;
   const bool contig = ldx == K;
@@ -169,7 +171,8 @@ __device__ __forceinline__ u32x2 int8_pack8(u32x4 a, float inv) {
 template <int VPL>
 __global__ void __launch_bounds__(256)
 int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                   int8_t* __restrict__ q, float* __restrict__ scale) {
+                   int8_t* __restrict__ q, float* __restrict__ scale, Gate gate) {
+  if (gated_off(gate)) return;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -218,6 +221,7 @@ size_t nvfp4_quant_ws_bytes(int64_t, int64_t) { return kAmaxBlocks * sizeof(floa
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                               uint8_t* q, uint8_t* scales, float* tscale, bool given,
                               void* ws, hipStream_t stream) {
+  const Gate gt = current_gate();
   float* partial = static_cast<float*>(ws);
   int nblk = 1;
   if (!given) {
@@ -226,10 +230,10 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
     nblk = (int)(work < kAmaxBlocks ? (work < 1 ? 1 : work) : kAmaxBlocks);
     if (contig)
       hipLaunchKernelGGL(nvfp4_amax_kernel<true>, dim3(nblk), dim3(256), 0, stream, x, M, K,
-                         ldx, partial);
+                         ldx, partial, gt);
     else
       hipLaunchKernelGGL(nvfp4_amax_kernel<false>, dim3(nblk), dim3(256), 0, stream, x, M, K,
-                         ldx, partial);
+                         ldx, partial, gt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -237,26 +241,27 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
   if (eblk > kEncBlocks) eblk = kEncBlocks;
   if (eblk < 1) eblk = 1;
   hipLaunchKernelGGL(nvfp4_encode_vec_kernel<kEncU>, dim3((unsigned)eblk), dim3(256), 0, stream,
-                     x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0);
+                     x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0, gt);
   return hipGetLastError();
 }
 
 hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                              float* scale, hipStream_t stream) {
+  const Gate gt = current_gate();
   const dim3 g((unsigned)((M + 3) / 4)), t(256);
   const int64_t vpl = (K / 8 + 63) / 64;
   if (vpl <= 1)
-    hipLaunchKernelGGL(int8_encode_kernel<1>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<1>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else if (vpl <= 2)
-    hipLaunchKernelGGL(int8_encode_kernel<2>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<2>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else if (vpl <= 4)
-    hipLaunchKernelGGL(int8_encode_kernel<4>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<4>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else if (vpl <= 8)
-    hipLaunchKernelGGL(int8_encode_kernel<8>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<8>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else if (vpl <= 16)
-    hipLaunchKernelGGL(int8_encode_kernel<16>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<16>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else
-    hipLaunchKernelGGL(int8_encode_kernel<0>, g, t, 0, stream, x, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(int8_encode_kernel<0>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qact_internal.h"
+
 namespace qact {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -90,6 +92,10 @@ __device__ __forceinline__ int e2m1_twice(uint32_t c) {
   const int mag = (int)((0xC8643210u >> ((c & 7u) * 4u)) & 0xFu);   // 0,1,2,3,4,6,8,12
   return (c & 8u) ? -mag : mag;
 }
+
+// True when the call's gate is closed: its kernels then return at once.
+// (One uniform byte load; every kernel of a gated call checks it first.)
+__device__ __forceinline__ bool gated_off(Gate g) { return g.flags && (*g.flags & g.bits) == 0u; }
 
 // Wave-level (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {

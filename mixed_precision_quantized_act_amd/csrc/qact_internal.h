@@ -7,6 +7,29 @@
 
 namespace qact {
 
+// Device-side gate of a call: every kernel of the call reads the byte
+// *flags on the device and does nothing unless (*flags & bits) != 0.
+// flags == nullptr: no gate.  Set per host thread through qa_set_gate.
+struct Gate {
+  const uint8_t* flags;
+  uint32_t bits;
+};
+Gate current_gate();
+
+// Gate bits written by the device-side decisions (launch_decide): per
+// linear, which activation format runs (none when its block is skipped);
+// per block, the compute path with ring slot `last` = 0 or 1 (the Delta
+// cache reads slot last and writes slot last ^ 1) or the skip path reading
+// slot last.
+enum : uint32_t {
+  kRouteNvfp4 = 1u, kRouteInt8 = 2u,
+  kBlkRun0 = 1u, kBlkRun1 = 2u, kBlkSkip0 = 4u, kBlkSkip1 = 8u
+};
+hipError_t launch_decide(const double* sums, const float* alpha, const float* beta, double tau,
+                         double delta, int L, int J, int* t_ctr, uint8_t* bstate, double* d_prev,
+                         uint8_t* blk_flags, uint8_t* lin_flags, uint8_t* mask_out,
+                         uint8_t* skip_out, hipStream_t stream);
+
 // ---- activation quantization (act_quant.hip)
 size_t nvfp4_quant_ws_bytes(int64_t M, int64_t K);
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

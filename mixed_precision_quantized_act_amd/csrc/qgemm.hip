@@ -107,7 +107,8 @@ static inline int64_t units_of(int64_t K) { return (K + kUnitK - 1) / kUnitK; }
 __global__ void __launch_bounds__(256)
 scale_tiles_kernel(const uint8_t* __restrict__ s0, int64_t rows0, uint32_t* __restrict__ dst0,
                    int tiles0, const uint8_t* __restrict__ s1, int64_t rows1,
-                   uint32_t* __restrict__ dst1, int64_t K, int units) {
+                   uint32_t* __restrict__ dst1, int64_t K, int units, Gate gate) {
+  if (gated_off(gate)) return;
   int tu = (int)blockIdx.x;
   const bool second = tu >= tiles0 * units;
   if (second) tu -= tiles0 * units;
@@ -188,6 +189,7 @@ struct GemmArgs {
   int splits;            // K slices per tail tile (1: no split)
   int split_units;       // raw units per slice (the last slice may have fewer)
   float* part;           // slice partial sums, kPartTile floats per (tail tile, slice)
+  Gate gate;             // the call's device-side gate
 };
 // fp32 partial sums of one tile: 4 waves x 256 accumulators x 64 lanes
 static constexpr int kPartTile = 4 * 256 * 64;
@@ -284,6 +286,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   using R = Raw<I8>;
   using AW = typename RawWords<I8>::A;
   __shared__ __attribute__((aligned(16))) uint8_t smem[R::kSmem];
+  if (gated_off(g.gate)) return;
 
   // XCD-aware tile order: hardware deals workgroups to the 8 XCDs in turn;
   // give each XCD a contiguous range of logical tiles, grouped kGroupM
@@ -938,7 +941,7 @@ static hipError_t launch_scale_tiles(const uint8_t* s0, int64_t rows0, uint32_t*
   const int64_t units = units_of(K);
   const int64_t t0 = (rows0 + kTileM - 1) / kTileM, t1 = s1 ? (rows1 + kTileM - 1) / kTileM : 0;
   hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)((t0 + t1) * units)), dim3(256), 0, st, s0,
-                     rows0, dst0, (int)t0, s1, rows1, dst1, K, (int)units);
+                     rows0, dst0, (int)t0, s1, rows1, dst1, K, (int)units, current_gate());
   return hipGetLastError();
 }
 
@@ -996,6 +999,7 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
 // split: the workspace region of the K split (null: no split)
 static GemmArgs base_args(int64_t M, int64_t N, int64_t K, uint8_t* split) {
   GemmArgs g = {};
+  g.gate = current_gate();
   g.K = K;
   g.units = (int)units_of(K);
   g.nk = (int)((K + kStageK - 1) / kStageK);

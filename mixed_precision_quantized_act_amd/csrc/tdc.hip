@@ -86,7 +86,8 @@ template <int MODE, bool PREV>
 __global__ void __launch_bounds__(kThreads)
 tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
            const uint16_t* __restrict__ prev, uint16_t* dst, int64_t n,
-           double* __restrict__ partial, int want_sums) {
+           double* __restrict__ partial, int want_sums, Gate gate) {
+  if (gated_off(gate)) return;
   Acc4 a = {{0.0, 0.0, 0.0, 0.0}};
   const int64_t nvec = n / 8;
   // kUnroll vectors per thread and sweep: all loads issued before any use
@@ -149,7 +150,8 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
 // order.
 __global__ void __launch_bounds__(kThreads)
 tdc_finalize_kernel(const double* __restrict__ partial, int rows, int ncols,
-                    double* __restrict__ sums) {
+                    double* __restrict__ sums, Gate gate) {
+  if (gated_off(gate)) return;
   __shared__ double red[4][kThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
@@ -181,10 +183,74 @@ tdc_finalize_kernel(const double* __restrict__ partial, int rows, int ncols,
   }
 }
 
+// One timestep's decisions on the device, from the sums the previous
+// step's calls left: for each block l (one thread each), first the state
+// update the host loop makes after a step -- Gamma_{t-1} = S1/S2 of the
+// block (tdc_update's or, for a skipped block, tdc_apply's), and for a
+// block computed at t-1 its Delta going to the other ring slot and d =
+// sqrt(S3)/sqrt(S4) once two Deltas are stored -- then the decisions of the
+// DMPQ rule (p = alpha Gamma + beta > tau: INT8, ties NVFP4, all INT8 at t
+// = 0; 6Bit-Diffusion, Fig. 3 caption) and of the TDC rule (skip when t >=
+// 2, the block ran at t-1 and d < delta; abstract and Fig. 4 caption), and
+// the gate bytes of the step's calls.  The step counter is advanced by
+// thread 0 after every block's update.
+__device__ __forceinline__ double ratio0_dev(double num, double den) {
+  if (den == 0.0) return num == 0.0 ? 0.0 : __longlong_as_double(0x7FF0000000000000ll);
+  return num / den;
+}
+
+__global__ void __launch_bounds__(kThreads)
+decide_kernel(const double* __restrict__ sums, const float* __restrict__ alpha,
+              const float* __restrict__ beta, double tau, double delta, int L, int J,
+              int* __restrict__ t_ctr, uint8_t* __restrict__ bstate, double* __restrict__ d_prev,
+              uint8_t* __restrict__ blk_flags, uint8_t* __restrict__ lin_flags,
+              uint8_t* __restrict__ mask_out, uint8_t* __restrict__ skip_out) {
+  const int t = *t_ctr;
+  for (int l = threadIdx.x; l < L; l += blockDim.x) {
+    uint32_t computed = bstate[4 * l], nst = bstate[4 * l + 1], last = bstate[4 * l + 2];
+    double gamma = 0.0;
+    if (t >= 1) {
+      const double* sl = sums + 4 * (int64_t)l;
+      gamma = ratio0_dev(sl[0], sl[1]);
+      if (computed) {
+        last ^= 1u;
+        nst = nst < 2u ? nst + 1u : 2u;
+        d_prev[l] = nst >= 2u ? ratio0_dev(sqrt(sl[2]), sqrt(sl[3]))
+                              : __longlong_as_double(0x7FF0000000000000ll);
+      }
+    }
+    const bool skip = t >= 2 && computed && d_prev[l] < delta;
+    for (int j = 0; j < J; ++j) {
+      const int i = l * J + j;
+      const double p = (double)alpha[i] * gamma + (double)beta[i];
+      const uint32_t m = (t == 0 || p > tau) ? 1u : 0u;   // 1: INT8
+      lin_flags[i] = (uint8_t)(skip ? 0u : (m ? kRouteInt8 : kRouteNvfp4));
+      if (mask_out) mask_out[i] = (uint8_t)m;
+    }
+    blk_flags[l] = (uint8_t)(skip ? (last ? kBlkSkip1 : kBlkSkip0) : (last ? kBlkRun1 : kBlkRun0));
+    if (skip_out) skip_out[l] = skip ? 1 : 0;
+    bstate[4 * l] = skip ? 0 : 1;
+    bstate[4 * l + 1] = (uint8_t)nst;
+    bstate[4 * l + 2] = (uint8_t)last;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *t_ctr = t + 1;
+}
+
+hipError_t launch_decide(const double* sums, const float* alpha, const float* beta, double tau,
+                         double delta, int L, int J, int* t_ctr, uint8_t* bstate, double* d_prev,
+                         uint8_t* blk_flags, uint8_t* lin_flags, uint8_t* mask_out,
+                         uint8_t* skip_out, hipStream_t stream) {
+  hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(kThreads), 0, stream, sums, alpha, beta, tau,
+                     delta, L, J, t_ctr, bstate, d_prev, blk_flags, lin_flags, mask_out, skip_out);
+  return hipGetLastError();
+}
+
 size_t reduce_ws_bytes(int64_t) { return (size_t)kRedBlocks * 4 * sizeof(double); }
 
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* prev,
                       uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream) {
+  const Gate gt = current_gate();
   const int64_t nvec = n / 8;
   int64_t nb = (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   if (nb > kRedBlocks) nb = kRedBlocks;
@@ -194,26 +260,26 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   const dim3 g((unsigned)nb), t(kThreads);
   if (mode == MODE_GAMMA)
     hipLaunchKernelGGL((tdc_kernel<MODE_GAMMA, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   else if (mode == MODE_UPDATE && prev)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, true>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   else if (mode == MODE_UPDATE)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   else if (mode == MODE_APPLY)
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   else if (mode == MODE_RELERR)
     hipLaunchKernelGGL((tdc_kernel<MODE_RELERR, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   else
     hipLaunchKernelGGL((tdc_kernel<MODE_COS, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want);
+                       partial, want, gt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !want) return e;
   const int ncols = mode == MODE_UPDATE ? 4 : mode == MODE_COS ? 3 : 2;
-  hipLaunchKernelGGL(tdc_finalize_kernel, dim3(1), t, 0, stream, partial, (int)nb, ncols, sums);
+  hipLaunchKernelGGL(tdc_finalize_kernel, dim3(1), t, 0, stream, partial, (int)nb, ncols, sums, gt);
   return hipGetLastError();
 }
 
