@@ -217,3 +217,17 @@ def test_cosine_helpers_match_oracle():
                                       T.tdc_decide_cos(t, c, cp, 0.9))
     assert _status("delta_cosine", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
     assert _status("delta_cosine", FAKE, FAKE, 64, FAKE, None, 0, None) == -5
+
+
+def test_step_control_validation():
+    # a gate needs bits; clearing takes none; decisions check shapes,
+    # pointers and alignment before any launch
+    assert _status("qa_set_gate", FAKE, 0) == -1
+    assert _status("qa_set_gate", None, 0) == 0
+    ok = [FAKE, FAKE, FAKE, 0.5, 0.05]
+    st = [FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None]
+    assert _status("qa_decide_step", *ok, 0, 4, *st) == -2
+    assert _status("qa_decide_step", *ok, 4, 0, *st) == -2
+    assert _status("qa_decide_step", None, *ok[1:], 4, 4, *st) == -1
+    assert _status("qa_decide_step", *ok, 4, 4, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == -1
+    assert _status("qa_decide_step", ctypes.c_void_p(FAKE.value + 4), *ok[1:], 4, 4, *st) == -3

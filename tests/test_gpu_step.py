@@ -270,3 +270,70 @@ def test_device_decisions_eager_and_graph(delta):
         np.testing.assert_array_equal(host(st.mask_out), ref[step][0], err_msg=f"graph mask, step {step}")
         np.testing.assert_array_equal(host(st.skip_out), ref[step][1], err_msg=f"graph skip, step {step}")
         np.testing.assert_array_equal(host(st.outs[-1]), ref[step][2], err_msg=f"graph output, step {step}")
+
+
+def test_decide_step_against_oracle_rules():
+    # qa_decide_step over 7 steps on sums set by hand (zero denominators,
+    # a prediction equal to tau, a distance equal to delta), against the
+    # oracle's rules driven by the host loop's state update
+    from oracle import tdc as T
+    qa, t = _qa(), torch()
+    L_, J_ = 6, 4
+    alpha = np.array([1.0, 2.0, 0.5, 1.0] * L_, np.float32)
+    beta = np.array([2.0 ** -7, 0.0, 0.1, -0.2] * L_, np.float32)
+    tau, delta = 0.2578125, 0.25          # Gamma 0.25: 0.25 + 2^-7 = tau (a tie)
+    rng = np.random.default_rng(4)
+    # per step, per block: (S1, S2, S3, S4)
+    special = [(1.0, 4.0, 1.0 / 16, 1.0),     # Gamma 0.25, d 0.25 = delta (not below)
+               (0.0, 0.0, 0.0, 0.0),          # Gamma 0/0 = 0, d 0/0 = 0
+               (3.0, 0.0, 2.0, 0.0),          # Gamma x/0 = inf, d x/0 = inf
+               (0.5, 4.0, 1.0 / 64, 1.0)]     # Gamma 0.125, d 0.125
+    steps = 7
+    sums_seq = []
+    for s_ in range(steps):
+        rows = []
+        for l in range(L_):
+            if (l + s_) % 3 == 0:
+                rows.append(special[(l + s_) % 4])
+            else:
+                rows.append(tuple(float(v) for v in rng.uniform(0.0, 1.0, 4)))
+        sums_seq.append(np.array(rows, np.float64))
+    sums = t.zeros((L_, 4), dtype=t.float64, device="cuda")
+    t_ctr = t.zeros(1, dtype=t.int32, device="cuda")
+    bstate = t.zeros((L_, 4), dtype=t.uint8, device="cuda")
+    d_prev = t.zeros(L_, dtype=t.float64, device="cuda")
+    blk = t.zeros(L_, dtype=t.uint8, device="cuda")
+    lin = t.zeros(L_ * J_, dtype=t.uint8, device="cuda")
+    mask_o = t.zeros(L_ * J_, dtype=t.uint8, device="cuda")
+    skip_o = t.zeros(L_, dtype=t.uint8, device="cuda")
+    # the host loop's state
+    computed = np.zeros(L_, bool)
+    n_st = np.zeros(L_, int)
+    last = np.zeros(L_, int)
+    dp = np.full(L_, math.inf)
+    gamma_prev = None
+    for step in range(steps):
+        qa.decide_step(sums, dev(alpha), dev(beta), tau, delta, L_, J_, t_ctr, bstate, d_prev,
+                       blk, lin, mask_o, skip_o)
+        t.cuda.synchronize()
+        if step >= 1:
+            prev = sums_seq[step - 1]
+            gamma_prev = np.array([T.ratio(prev[l, 0], prev[l, 1]) for l in range(L_)])
+            for l in range(L_):
+                if computed[l]:
+                    last[l] ^= 1
+                    n_st[l] = min(n_st[l] + 1, 2)
+                    dp[l] = T.rel_l2(prev[l, 2], prev[l, 3]) if n_st[l] >= 2 else math.inf
+        mask = T.dmpq_mask(gamma_prev, alpha, beta, tau, J_)
+        skip = T.tdc_decide(step, dp, computed, delta)
+        np.testing.assert_array_equal(host(mask_o), mask, err_msg=f"mask, step {step}")
+        np.testing.assert_array_equal(host(skip_o), skip, err_msg=f"skip, step {step}")
+        want_lin = np.where(np.repeat(skip, J_) == 1, 0, np.where(mask == 1, 2, 1))
+        np.testing.assert_array_equal(host(lin), want_lin.astype(np.uint8))
+        want_blk = np.where(skip == 1, np.where(last == 1, 8, 4), np.where(last == 1, 2, 1))
+        np.testing.assert_array_equal(host(blk), want_blk.astype(np.uint8))
+        np.testing.assert_array_equal(host(d_prev)[computed | (n_st > 0)],
+                                      dp[computed | (n_st > 0)])
+        computed = skip == 0
+        sums.copy_(t.from_numpy(sums_seq[step]))
+    assert int(host(t_ctr)[0]) == steps
