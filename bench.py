@@ -163,7 +163,8 @@ def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
 
 
 def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, steps=10,
-                  delta=0.05, cfg=4, modes=("w4a8", "w4a4", "dmpq", "full", "median", "cos")):
+                  delta=0.05, cfg=4,
+                  modes=("w4a8", "w4a4", "dmpq", "full", "median", "cos", "device")):
     """The CogVideoX-2B-shaped stack (30 blocks; per block the four internal
     linears QKV H->3H, O H->H, up H->F with GELU, down F->H; attention
     replaced by its value slice, no token mixing) over `steps` drifting
@@ -209,7 +210,7 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     beta = np.full(L * J, 0.01, np.float32)
     i16 = lambda t: t.view(torch.int16)
 
-    def linear(fmt, x, ldx, lay, y, gelu):
+    def linear(fmt, x, ldx, lay, y, gelu, stream=stream):
         q, sc, ts, N, K = lay
         xv = torch.as_strided(x, (M, K), (ldx, 1))
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
@@ -311,13 +312,110 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                 "int8_share": round(float(np.mean(int8_share[2:])), 3),
                 "skipped_blocks": int(skipped), "blocks_run": L * steps, "delta": delta,
                 "d_median": round(float(np.median(d_seen)), 4) if d_seen else None,
-                "cos_median": round(float(np.median(cos_seen)), 4) if cos_seen else None}
+                "cos_median": round(float(np.median(cos_seen)), 4) if cos_seen else None,
+                "tau": tau}
+
+    outs = None
+
+    def run_device(tau, delta, graph):
+        """DMPQ + TDC with the decisions made on the device
+        (qa.decide_step) and every path enqueued under its gate: no host
+        sync inside a step; graph: one step captured as a HIP graph and
+        replayed.  Mean ms/step of steps 2.. (one sync around them)."""
+        nonlocal outs
+        if outs is None:
+            outs = [torch.empty((M, H), dtype=bf, device=dev) for _ in range(L)]
+        alpha_d = torch.from_numpy(alpha).to(dev)
+        beta_d = torch.from_numpy(beta).to(dev)
+        t_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+        bstate = torch.zeros((L, 4), dtype=torch.uint8, device=dev)
+        d_dev = torch.zeros(L, dtype=torch.float64, device=dev)
+        blk = torch.zeros(L, dtype=torch.uint8, device=dev)
+        lin = torch.zeros(L * J, dtype=torch.uint8, device=dev)
+        skip_o = torch.zeros(L, dtype=torch.uint8, device=dev)
+        x_in = torch.empty((M, H), dtype=bf, device=dev)
+
+        def reset():
+            for r in ring:
+                for b in r:
+                    b.zero_()
+            for b in (sums, t_ctr, bstate, d_dev):
+                b.zero_()
+
+        def gated_linear(j, l, x, ldx, y, gelu, stream):
+            for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
+                with qa.gate(lin[l * J + j:], bit):
+                    linear(fmt, x, ldx, layers[l][j], y, gelu, stream=stream)
+
+        def step(stream):
+            qa.decide_step(sums, alpha_d, beta_d, tau, delta, L, J, t_ctr, bstate, d_dev, blk,
+                           lin, None, skip_o, stream=stream)
+            cur = x_in
+            for l in range(L):
+                out = outs[l]
+                r0, r1 = ring[l]
+                for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
+                    with qa.gate(blk[l:], bit):
+                        qa.tdc_apply(i16(cur), i16(slot), i16(out), sums[l, :2], rws, stream=stream)
+                gated_linear(0, l, cur, H, qkv, False, stream)
+                gated_linear(1, l, qkv.view(-1)[2 * H:], 3 * H, o, False, stream)
+                with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
+                    qa.tdc_apply(i16(cur), i16(o), i16(x1), stream=stream)
+                gated_linear(2, l, x1, H, u, True, stream)
+                gated_linear(3, l, u, F_, dd, False, stream)
+                with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
+                    qa.tdc_apply(i16(x1), i16(dd), i16(out), stream=stream)
+                for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
+                    with qa.gate(blk[l:], bit):
+                        qa.tdc_update(i16(cur), i16(out), i16(prev), i16(nxt), sums[l], rws,
+                                      stream=stream)
+                cur = out
+
+        g = None
+        if graph:
+            s = torch.cuda.Stream(device=dev)
+            s.wait_stream(torch.cuda.current_stream(dev))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    step(s.cuda_stream)        # every launch on the capturing stream
+            torch.cuda.current_stream(dev).wait_stream(s)
+        reset()
+        skip_acc = torch.zeros(L, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        t0 = None
+        for t in range(steps):
+            if t == 2:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            x_in.copy_(xs[t])
+            if graph:
+                g.replay()
+            else:
+                step(stream)
+            skip_acc += skip_o            # (enqueued: no sync)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del g
+        return {"ms_per_step": round(1e3 * dt / (steps - 2), 2), "delta": delta,
+                "skipped_blocks": int(skip_acc.sum().item()), "blocks_run": L * steps,
+                "decisions": "device", "graph": graph}
 
     res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full") if m in modes}
     # the synthetic trajectory's block updates change by d ~ d_median from
     # step to step; a threshold at that median shows the skip path's speed
     if "median" in modes and res["dmpq"]["d_median"]:
         res["full_delta_at_median_d"] = run("full", delta=res["dmpq"]["d_median"])
+    # the same two configurations with the decisions on the device (no
+    # per-step host sync), enqueued per step and as a replayed graph
+    if "device" in modes and "full" in res:
+        tau_d = res["dmpq"]["tau"]
+        res["full_device"] = run_device(tau_d, delta, graph=False)
+        res["full_device_graph"] = run_device(tau_d, delta, graph=True)
+        if "full_delta_at_median_d" in res:
+            dm = res["dmpq"]["d_median"]
+            res["full_delta_at_median_d_device"] = run_device(tau_d, dm, graph=False)
+            res["full_delta_at_median_d_device_graph"] = run_device(tau_d, dm, graph=True)
     # the cosine rule of Fig. 4 (a variant): threshold at the median cosine
     # of the DMPQ run's successive Deltas (an untimed probe run)
     if "cos" in modes:
@@ -579,10 +677,19 @@ def main():
     stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
              if args.stack_steps > 0 else None)
     layers2b = layer_rates(qa, torch, np, dev, stream, M, 1920, 7680)
+    # a launch-bound stack (30 blocks of the single-linear config's width:
+    # H 256, FFN 1024, 256 tokens), where the per-step host sync and the
+    # launches, not the kernels, set the step time
+    small = None
+    if args.stack_steps > 0:
+        small = stack_section(qa, torch, np, dev, stream, L=30, H=256, F_=1024, M=256,
+                              steps=args.stack_steps, cfg=1,
+                              modes=("dmpq", "full", "median", "device"))
     stack5 = None
     if args.stack5_steps > 0:
         stack5 = stack_section(qa, torch, np, dev, stream, L=42, H=3072, F_=12288, M=M,
-                               steps=args.stack5_steps, cfg=5, modes=("dmpq", "full", "median"))
+                               steps=args.stack5_steps, cfg=5,
+                               modes=("dmpq", "full", "median", "device"))
         stack5["per_layer_qlinear"] = layer_rates(qa, torch, np, dev, stream, M, 3072, 12288)
 
     ms_step = wall * 1e3 / args.steps
@@ -643,6 +750,7 @@ def main():
         "stack_cogvideox2b_shape": stack,
         "per_layer_qlinear_cogvideox2b_shape": layers2b,
         "stack_cogvideox5b_shape": stack5,
+        "stack_launch_bound_256_tokens": small,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
