@@ -448,6 +448,8 @@ def main():
                     help="timesteps of the 30-block stack section (0 skips it)")
     ap.add_argument("--stack5-steps", type=int, default=10,
                     help="timesteps of the 42-block 5B-shaped stack section (0 skips it)")
+    ap.add_argument("--layer-reps", type=int, default=5,
+                    help="timed calls per linear of the per-layer qlinear section (0 skips it)")
     ap.add_argument("--cold-reps", type=int, default=9,
                     help="reps of each bandwidth kernel timed after a 1 GiB cache-evicting read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -676,7 +678,8 @@ def main():
     del h, hq, hs
     stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
              if args.stack_steps > 0 else None)
-    layers2b = layer_rates(qa, torch, np, dev, stream, M, 1920, 7680)
+    layers2b = (layer_rates(qa, torch, np, dev, stream, M, 1920, 7680, reps=args.layer_reps)
+                if args.layer_reps > 0 else None)
     # a launch-bound stack (30 blocks of the single-linear config's width:
     # H 256, FFN 1024, 256 tokens), where the per-step host sync and the
     # launches, not the kernels, set the step time
@@ -690,7 +693,9 @@ def main():
         stack5 = stack_section(qa, torch, np, dev, stream, L=42, H=3072, F_=12288, M=M,
                                steps=args.stack5_steps, cfg=5,
                                modes=("dmpq", "full", "median", "device"))
-        stack5["per_layer_qlinear"] = layer_rates(qa, torch, np, dev, stream, M, 3072, 12288)
+        if args.layer_reps > 0:
+            stack5["per_layer_qlinear"] = layer_rates(qa, torch, np, dev, stream, M, 3072, 12288,
+                                                      reps=args.layer_reps)
 
     ms_step = wall * 1e3 / args.steps
     flops_step = 2 * 2.0 * M * N * K
