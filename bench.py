@@ -162,6 +162,95 @@ def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
     return out
 
 
+def ffn_section(qa, torch, np, dev, stream, reps=5):
+    """The FFN config: 17776 tokens of Student-t(3) activations, 1920 ->
+    7680 (GELU-tanh) -> 1920 with NVFP4 weights; a forward pass (activation
+    quantization and GEMM of both linears) in each combination of the two
+    formats, and the DMPQ choice for it: p_l = 1.0 Gamma_l + 0.01 per linear
+    with Gamma_l of a synthetic in/out pair of the linear's input (out = in +
+    0.1 N(0,1), block_gamma), tau at the midpoint so that one of the two
+    linears is INT8."""
+    import synth
+    x, wu, wd = synth.ffn_case(3)
+    M, K = x.shape
+    F_ = wu.shape[0]
+    to = lambda a: torch.from_numpy(a.view(np.int16).copy()).to(dev)
+    xd = to(x)
+    ws = []
+    for w in (wu, wd):
+        N, KK = w.shape
+        q, sc, ts = qa.empty_nvfp4(N, KK, dev)
+        qa.act_quant(qa.NVFP4, to(w), q, sc, ts, 0,
+                     qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, KK), dev), stream=stream)
+        ws.append((q, sc, ts, N, KK))
+    h = torch.empty((M, F_), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    a4 = qa.empty_nvfp4(M, F_, dev)
+    a8 = qa.empty_int8_act(M, F_, dev)
+    qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
+    gws = qa.workspace(max(qa.qlinear_workspace(f, M, w[3], w[4]) for f in (qa.NVFP4, qa.INT8)
+                           for w in ws), dev)
+
+    def lin(fmt, xin, w, out, gelu):
+        q, sc, ts, N, KK = w
+        epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+        if fmt == 0:
+            aq = a4[0].view(-1)[: M * KK // 2].view(M, KK // 2)
+            asc = a4[1].view(-1)[: M * KK // 16].view(M, KK // 16)
+            qa.act_quant(qa.NVFP4, xin, aq, asc, a4[2], 0, qws, stream=stream)
+            qa.qlinear_nvfp4(aq, asc, a4[2], q, sc, ts, out, M, N, KK, epi=epi, ws=gws,
+                             stream=stream)
+        else:
+            aq = a8[0].view(-1)[: M * KK].view(M, KK)
+            qa.act_quant(qa.INT8, xin, aq, a8[1], stream=stream)
+            qa.qlinear_int8(aq, a8[1], q, sc, ts, out, M, N, KK, epi=epi, ws=gws, stream=stream)
+
+    def ffn(fu, fd):
+        lin(fu, xd, ws[0], h, True)
+        lin(fd, h.view(torch.int16), ws[1], y, False)
+
+    flops = 2.0 * M * K * F_ * 2
+    res = {}
+    for fu in (0, 1):
+        for fd in (0, 1):
+            ffn(fu, fd)
+            ts_ = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ffn(fu, fd)
+                e1.record()
+                e1.synchronize()
+                ts_.append(e0.elapsed_time(e1))
+            ms = float(np.median(ts_))
+            name = f"up_{'int8' if fu else 'nvfp4'}_down_{'int8' if fd else 'nvfp4'}"
+            res[name] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    # DMPQ choice for the two linears
+    rws = qa.workspace(qa.reduce_workspace(M * F_), dev)
+    gam = []
+    g2 = torch.zeros(2, dtype=torch.float64, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(303)
+    for xin in (xd, h.view(torch.int16)):
+        xf = xin.view(torch.bfloat16).float()
+        out = (xf + 0.1 * torch.randn(xf.shape, generator=gen, device=dev)).to(torch.bfloat16)
+        qa.block_gamma(xin.reshape(-1), out.view(torch.int16).reshape(-1), g2, rws, stream=stream)
+        gam.append(qa.gamma_from_sums(g2.cpu().numpy()))
+        del xf, out
+    alpha = np.full(2, 1.0, np.float32)
+    beta = np.full(2, 0.01, np.float32)
+    p = np.array(gam) * 1.0 + 0.01
+    tau = float(0.5 * (p.min() + p.max()))
+    mask = qa.dmpq_mask(np.array(gam), alpha, beta, tau, 2, 1)
+    res["dmpq"] = {"gamma": [round(float(g), 5) for g in gam], "tau": round(tau, 6),
+                   "mask_int8": [int(m) for m in mask],
+                   "pass": f"up_{'int8' if mask[0] else 'nvfp4'}_down_{'int8' if mask[1] else 'nvfp4'}"}
+    res["config"] = {"tokens": M, "hidden": K, "ffn": F_, "activations": "Student-t(3) bf16",
+                     "GFLOP_per_pass": round(flops / 1e9, 1)}
+    del h, y, a4, a8, gws, qws
+    return res
+
+
 def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, steps=10,
                   delta=0.05, cfg=4,
                   modes=("w4a8", "w4a4", "dmpq", "full", "median", "cos", "device")):
@@ -678,6 +767,7 @@ def main():
     del h, hq, hs
     stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
              if args.stack_steps > 0 else None)
+    ffn3 = ffn_section(qa, torch, np, dev, stream) if args.layer_reps > 0 else None
     layers2b = (layer_rates(qa, torch, np, dev, stream, M, 1920, 7680, reps=args.layer_reps)
                 if args.layer_reps > 0 else None)
     # a launch-bound stack (30 blocks of the single-linear config's width:
@@ -754,6 +844,7 @@ def main():
         "ffn_up_fused_nvfp4_output": ffn_fused,
         "stack_cogvideox2b_shape": stack,
         "per_layer_qlinear_cogvideox2b_shape": layers2b,
+        "ffn_student_t": ffn3,
         "stack_cogvideox5b_shape": stack5,
         "stack_launch_bound_256_tokens": small,
         "roofline": roofline,
