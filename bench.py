@@ -209,6 +209,33 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
         lin(fu, xd, ws[0], h, True)
         lin(fd, h.view(torch.int16), ws[1], y, False)
 
+    amax_word = qws[:4].view(torch.int32)
+
+    def ffn_amax(fu):
+        # NVFP4 down projection whose tensor amax comes from the up GEMM's
+        # epilogue (qlinear_*_amax into act_quant's workspace, QA_AMAX_GIVEN)
+        amax_word.zero_()
+        q, sc, ts, N, KK = ws[0]
+        if fu == 0:
+            aq = a4[0].view(-1)[: M * K // 2].view(M, K // 2)
+            asc = a4[1].view(-1)[: M * K // 16].view(M, K // 16)
+            xws = qa.workspace(4096, dev) if not hasattr(ffn_amax, "xws") else ffn_amax.xws
+            ffn_amax.xws = xws
+            qa.act_quant(qa.NVFP4, xd, aq, asc, a4[2], 0, xws, stream=stream)
+            qa.qlinear_nvfp4_amax(aq, asc, a4[2], q, sc, ts, h, amax_word, M, N, KK,
+                                  epi=qa.EPI_GELU_TANH, ws=gws, stream=stream)
+        else:
+            aq = a8[0].view(-1)[: M * K].view(M, K)
+            qa.act_quant(qa.INT8, xd, aq, a8[1], stream=stream)
+            qa.qlinear_int8_amax(aq, a8[1], q, sc, ts, h, amax_word, M, N, KK,
+                                 epi=qa.EPI_GELU_TANH, ws=gws, stream=stream)
+        q, sc, ts, N, KK = ws[1]
+        aq = a4[0].view(-1)[: M * KK // 2].view(M, KK // 2)
+        asc = a4[1].view(-1)[: M * KK // 16].view(M, KK // 16)
+        qa.act_quant(qa.NVFP4, h.view(torch.int16), aq, asc, a4[2], qa.AMAX_GIVEN, qws,
+                     stream=stream)
+        qa.qlinear_nvfp4(aq, asc, a4[2], q, sc, ts, y, M, N, KK, ws=gws, stream=stream)
+
     flops = 2.0 * M * K * F_ * 2
     res = {}
     for fu in (0, 1):
@@ -225,6 +252,19 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
             ms = float(np.median(ts_))
             name = f"up_{'int8' if fu else 'nvfp4'}_down_{'int8' if fd else 'nvfp4'}"
             res[name] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    for fu in (0, 1):
+        ffn_amax(fu)
+        ts_ = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ffn_amax(fu)
+            e1.record()
+            e1.synchronize()
+            ts_.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts_))
+        name = f"up_{'int8' if fu else 'nvfp4'}_down_nvfp4_amax_from_up_epilogue"
+        res[name] = {"ms": round(ms, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
     # DMPQ choice for the two linears
     rws = qa.workspace(qa.reduce_workspace(M * F_), dev)
     gam = []

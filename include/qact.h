@@ -68,6 +68,11 @@ typedef enum { QA_EPI_NONE = 0, QA_EPI_GELU_TANH = 1 } qa_epi;
 /* NVFP4 only: *tscale is an input (a calibrated or producer-computed s_T)
  * and the tensor amax pass is skipped. */
 #define QA_TSCALE_GIVEN 1u
+/* NVFP4 only: the tensor |max| amax_T is already in the first 4 bytes of
+ * ws (float bits, as qlinear_nvfp4_amax / qlinear_int8_amax produce it);
+ * the amax pass is skipped and s_T = amax_T / 2688 is computed from it and
+ * written to *tscale -- the same s_T, bit for bit, as without the flag. */
+#define QA_AMAX_GIVEN 2u
 
 /* Human-readable name of a status code (static storage). */
 const char* qa_strerror(int status);
@@ -84,6 +89,7 @@ const char* qa_build_info(void);
  * q      NVFP4: u8 [M][K/2];  INT8: i8 [M][K]
  * scales NVFP4: u8 [M][K/16];  INT8: f32 [M]
  * tscale NVFP4: f32 device scalar, output (or input with QA_TSCALE_GIVEN);
+ *        QA_AMAX_GIVEN takes amax_T from ws (see above), needs ws 4-aligned;
  *        INT8: must be NULL
  * M >= 0 (M == 0 enqueues nothing), 0 < K, K % 16 == 0 for NVFP4.
  * ------------------------------------------------------------------------ */
@@ -157,6 +163,26 @@ int qlinear_int8(const int8_t* a_q, const float* a_s,
                  int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                  void* y, int64_t ldy, qa_out out, qa_epi epi,
                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* qlinear_nvfp4_amax / qlinear_int8_amax: qlinear_nvfp4 / qlinear_int8
+ * with a bf16 output (16-byte aligned, ldy % 4 == 0; otherwise
+ * QA_EUNSUPPORTED) whose |max| over the stored values is also taken in the
+ * GEMM epilogue and atomically max-combined into the device word *y_amax
+ * (float bits; the caller sets it to 0 before the call).  Point y_amax at
+ * the workspace of the act_quant NVFP4 call that quantizes y for the next
+ * linear and pass QA_AMAX_GIVEN there: that call then skips its read of the
+ * whole tensor for amax_T (6Bit-Diffusion, Fig. 2 caption: the consumer's
+ * activations are quantized per linear; the producer already holds every
+ * value).  y_amax must not overlap y, the inputs or ws. */
+int qlinear_nvfp4_amax(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                       const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M,
+                       int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
+                       qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                      const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
+                      const uint16_t* bias, void* y, int64_t ldy, qa_epi epi, uint32_t* y_amax,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* act_quant of x followed by the matching qlinear_* (one layer).  For
  * NVFP4 the tensor scale is computed from x (flags may hold

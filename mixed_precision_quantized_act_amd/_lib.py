@@ -14,6 +14,7 @@ NVFP4, INT8 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 EPI_NONE, EPI_GELU_TANH = 0, 1
 TSCALE_GIVEN = 1
+AMAX_GIVEN = 2
 
 
 class QactError(RuntimeError):
@@ -43,6 +44,10 @@ _SIGS = {
                                        _P, _P, _P, _P, _SZ, _P]),
     "qlinear_int8_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P,
                                       _P, _P, _P, _SZ, _P]),
+    "qlinear_nvfp4_amax": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
+                                          ctypes.c_int, _P, _P, _SZ, _P]),
+    "qlinear_int8_amax": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
+                                         ctypes.c_int, _P, _P, _SZ, _P]),
     "qlinear_layer_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _I64, _I64,
                                _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
@@ -166,6 +171,24 @@ def qlinear_int8_q(a_q, a_s, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bias=None,
     _check("qlinear_int8_q", lib().qlinear_int8_q(
         _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), epi,
         _ptr(y_ts), _ptr(y_q), _ptr(y_s), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def qlinear_nvfp4_amax(a_q, a_s, a_ts, w_q, w_s, w_ts, y, y_amax, M, N, K, bias=None,
+                       epi=EPI_NONE, ws=None, ldy=None, stream=None):
+    """qlinear_nvfp4 (bf16 out) that also max-combines |y| into y_amax."""
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("qlinear_nvfp4_amax", lib().qlinear_nvfp4_amax(
+        _ptr(a_q), _ptr(a_s), _ptr(a_ts), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias),
+        _ptr(y), ldy, epi, _ptr(y_amax), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def qlinear_int8_amax(a_q, a_s, w_q, w_s, w_ts, y, y_amax, M, N, K, bias=None, epi=EPI_NONE,
+                      ws=None, ldy=None, stream=None):
+    """qlinear_int8 (bf16 out) that also max-combines |y| into y_amax."""
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("qlinear_int8_amax", lib().qlinear_int8_amax(
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), _ptr(y), ldy,
+        epi, _ptr(y_amax), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def qlinear_layer_workspace(fmt, M, N, K):

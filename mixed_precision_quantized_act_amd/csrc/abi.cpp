@@ -43,6 +43,8 @@ int check_out(qa_out out, qa_epi epi) {
 
 // the calling thread's gate (qa_set_gate), applied to every launch it makes
 thread_local Gate g_gate = {nullptr, 0u};
+// set only for the duration of a qlinear_*_amax call: the output |max| target
+thread_local uint32_t* g_out_amax = nullptr;
 
 }  // namespace
 
@@ -83,7 +85,8 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   if (int s = check_mk(M, K)) return s;
   if (ldx < K || ldx % 8) return QA_ESHAPE;
   if (!aligned16(x) || !aligned16(q)) return QA_EALIGN;
-  if (flags & ~QA_TSCALE_GIVEN) return QA_EINVAL;
+  if (flags & ~(QA_TSCALE_GIVEN | QA_AMAX_GIVEN)) return QA_EINVAL;
+  if ((flags & QA_TSCALE_GIVEN) && (flags & QA_AMAX_GIVEN)) return QA_EINVAL;
   const size_t xbytes = M ? (size_t)((M - 1) * ldx + K) * 2 : 0;
   if (fmt == QA_INT8) {
     if (tscale || flags) return QA_EINVAL;
@@ -97,13 +100,16 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   if (!tscale) return QA_EINVAL;
   if (reinterpret_cast<uintptr_t>(tscale) & 3u) return QA_EALIGN;
   const bool given = (flags & QA_TSCALE_GIVEN) != 0;
+  const bool amax_given = (flags & QA_AMAX_GIVEN) != 0;
   if (!given && ws_bytes < nvfp4_quant_ws_bytes(M, K)) return QA_EWORKSPACE;
   if (!given && !ws) return QA_EINVAL;
+  if (amax_given && (reinterpret_cast<uintptr_t>(ws) & 3u)) return QA_EALIGN;
   if (overlap(x, xbytes, q, (size_t)(M * K / 2)) || overlap(x, xbytes, scales, (size_t)(M * K / 16)))
     return QA_EALIAS;
   if (M == 0) return QA_OK;
   return hip_status(launch_nvfp4_quant(x, M, K, ldx, static_cast<uint8_t*>(q),
-                                       static_cast<uint8_t*>(scales), tscale, given, ws, stream));
+                                       static_cast<uint8_t*>(scales), tscale, given, amax_given,
+                                       ws, stream));
 }
 
 // -------------------------------------------------------------- qlinear --
@@ -142,6 +148,7 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
+  o.y_amax = g_out_amax;
   return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
@@ -163,8 +170,55 @@ int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const 
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
+  o.y_amax = g_out_amax;
   return hip_status(
       launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
+}
+
+// bf16 output and its |max| (the tensor amax of a following NVFP4
+// act_quant, which then skips its amax pass: QA_AMAX_GIVEN)
+static int check_amax_out(const GemmOut& o, const uint32_t* y_amax, const void* y, size_t ybytes,
+                          const void* ws, size_t ws_bytes) {
+  if (!y_amax) return QA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(y_amax) & 3u) return QA_EALIGN;
+  if (!gemm_out_staged(o)) return QA_EUNSUPPORTED;
+  if (overlap(y, ybytes, y_amax, 4) || overlap(ws, ws_bytes, y_amax, 4)) return QA_EALIAS;
+  return QA_OK;
+}
+
+int qlinear_nvfp4_amax(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
+                       const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M,
+                       int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
+                       qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  GemmOut o = {y, ldy, 0, epi == QA_EPI_GELU_TANH, bias};
+  o.y_amax = y_amax;
+  if (y && ldy >= N && M > 0 && N > 0)
+    if (int s = check_amax_out(o, y_amax, y, (size_t)((M - 1) * ldy + N) * 2, ws, ws_bytes))
+      return s;
+  if (!y_amax) return QA_EINVAL;
+  g_out_amax = y_amax;
+  const int s = qlinear_nvfp4(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, bias, y, ldy, QA_OUT_BF16,
+                              epi, ws, ws_bytes, stream);
+  g_out_amax = nullptr;
+  return s;
+}
+
+int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                      const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
+                      const uint16_t* bias, void* y, int64_t ldy, qa_epi epi, uint32_t* y_amax,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  GemmOut o = {y, ldy, 0, epi == QA_EPI_GELU_TANH, bias};
+  o.y_amax = y_amax;
+  if (y && ldy >= N && M > 0 && N > 0)
+    if (int s = check_amax_out(o, y_amax, y, (size_t)((M - 1) * ldy + N) * 2, ws, ws_bytes))
+      return s;
+  if (!y_amax) return QA_EINVAL;
+  g_out_amax = y_amax;
+  const int s = qlinear_int8(a_q, a_s, w_q, w_s, w_ts, M, N, K, bias, y, ldy, QA_OUT_BF16, epi,
+                             ws, ws_bytes, stream);
+  g_out_amax = nullptr;
+  return s;
 }
 
 // NVFP4 output of the linear (activation quantization of its consumer,
@@ -246,7 +300,7 @@ int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t fl
   if (!aligned16(ws)) return QA_EALIGN;
   uint8_t* p = static_cast<uint8_t*>(ws);
   if (fmt == QA_NVFP4) {
-    if (!x_ts) return QA_EINVAL;
+    if (!x_ts || (flags & QA_AMAX_GIVEN)) return QA_EINVAL;   // its act_quant workspace is internal
     uint8_t* aq = p;
     p += round256((size_t)(M * K / 2));
     uint8_t* as = p;

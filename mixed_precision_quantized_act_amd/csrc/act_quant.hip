@@ -220,11 +220,11 @@ size_t nvfp4_quant_ws_bytes(int64_t, int64_t) { return kAmaxBlocks * sizeof(floa
 
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                               uint8_t* q, uint8_t* scales, float* tscale, bool given,
-                              void* ws, hipStream_t stream) {
+                              bool amax_given, void* ws, hipStream_t stream) {
   const Gate gt = current_gate();
   float* partial = static_cast<float*>(ws);
-  int nblk = 1;
-  if (!given) {
+  int nblk = 1;                  // amax_given: the one partial maximum is ws[0]
+  if (!given && !amax_given) {
     const bool contig = ldx == K;
     const int64_t work = contig ? (M * K / 8 + 256 * kUnroll - 1) / (256 * kUnroll) : M;
     nblk = (int)(work < kAmaxBlocks ? (work < 1 ? 1 : work) : kAmaxBlocks);

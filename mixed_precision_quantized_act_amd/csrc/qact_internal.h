@@ -32,9 +32,10 @@ hipError_t launch_decide(const double* sums, const float* alpha, const float* be
 
 // ---- activation quantization (act_quant.hip)
 size_t nvfp4_quant_ws_bytes(int64_t M, int64_t K);
+// amax_given: the tensor |max| is the float at ws[0] (no amax pass)
 hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                               uint8_t* q, uint8_t* scales, float* tscale, bool given,
-                              void* ws, hipStream_t stream);
+                              bool amax_given, void* ws, hipStream_t stream);
 hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                              float* scale, hipStream_t stream);
 
@@ -51,7 +52,11 @@ struct GemmOut {
   uint8_t* yq = nullptr;  // non-null: NVFP4 output (codes [M][N/2], scales [M][N/16])
   uint8_t* ys = nullptr;  //   quantized with the given tensor scale *y_ts instead of y
   const float* y_ts = nullptr;
+  uint32_t* y_amax = nullptr;  // bf16 staged output: atomic max of its |values| (float bits)
 };
+// true when the output takes the bf16 staged epilogue (the one that can
+// also produce the output's |max|)
+bool gemm_out_staged(const GemmOut& o);
 size_t nvfp4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                              const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,

@@ -153,6 +153,7 @@ struct EpiArgs {
   uint8_t* yq;           // NVFP4 output: codes [M][N/2], scales [M][N/16],
   uint8_t* ys;           // with the given tensor scale *y_ts
   const float* y_ts;
+  uint32_t* amax;        // bf16 staged output: |max| of the stored values (float bits), atomic max
 };
 
 // Epilogue kinds (one kernel each, so that the executed epilogue code stays
@@ -663,6 +664,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     constexpr bool kBias = kEpi == kEpiStagedBias || kEpi == kEpiStagedBiasGelu;
     constexpr bool kGelu = kEpi == kEpiStagedGelu || kEpi == kEpiStagedBiasGelu;
     uint8_t* const stg = smem + wave * 8192 * kPassTiles;
+    uint32_t amx = 0;        // |max| of this lane's stored values (bf16 patterns)
     // bias of the lane's 64 columns (columns past N read column N-1)
     float bv[kBias ? kFN : 1][4][4];
     if constexpr (kBias)
@@ -716,15 +718,28 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
         const int r = it * 4 + (lane >> 4);
         if (r < rows_left && k * 8 < cols_left) {
           uint16_t* yp = ybase + (int64_t)r * e.ldy + k * 8;
-          if (k * 8 + 8 <= cols_left)
+          if (k * 8 + 8 <= cols_left) {
             *reinterpret_cast<u32x4*>(yp) = d[it];
-          else
-            for (int t = 0; k * 8 + t < cols_left; ++t)
-              yp[t] = (uint16_t)(d[it][t >> 1] >> (16 * (t & 1)));
+            if (e.amax) amx = max(amx, fold_max(abs_max8_pk(d[it], u16x2{0, 0})));
+          } else {
+            for (int t = 0; k * 8 + t < cols_left; ++t) {
+              const uint32_t b = (d[it][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+              yp[t] = (uint16_t)b;
+              amx = max(amx, b & 0x7FFFu);
+            }
+          }
         }
       }
       // the next pass overwrites the slice after these reads (in order)
       asm volatile("" ::: "memory");
+    }
+    if (e.amax) {
+      // |bf16| patterns of the stored values order as the values do: the
+      // wave's integer maximum, then one atomic maximum per wave of its
+      // float bits (pattern << 16), as the act_quant amax pass reads them
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, o, 64));
+      if (lane == 0) atomicMax(e.amax, amx << 16);
     }
   } else if constexpr (kEpi == kEpiQuant) {
     // NVFP4 output with the given tensor scale s_T: every output is rounded
@@ -854,6 +869,8 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
 static int vec_ok(const GemmOut& o) {
   return (reinterpret_cast<uintptr_t>(o.y) % 16 == 0) && (o.ldy % 4 == 0);
 }
+
+bool gemm_out_staged(const GemmOut& o) { return !o.yq && !o.out_f32 && vec_ok(o); }
 
 static size_t scale_tiles_bytes(int64_t rows, int64_t K) {
   return (size_t)((rows + kTileM - 1) / kTileM) * (size_t)units_of(K) * 1024u;
@@ -1033,7 +1050,8 @@ hipError_t launch_nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_s, const float
   g.b = w_q;
   g.a_ts = a_ts;
   g.w_ts = w_ts;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts,
+               o.y_amax};
   return launch_gemm(false, g, e, st);
 }
 
@@ -1059,7 +1077,8 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
   g.b = w_q;
   g.w_ts = w_ts;
   g.a_rs = a_s;
-  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts};
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec_ok(o), o.yq, o.ys, o.y_ts,
+               o.y_amax};
   return launch_gemm(true, g, e, st);
 }
 

@@ -51,7 +51,12 @@ def test_act_quant_validation():
     assert _status("act_quant", 7, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -1
     assert _status("act_quant", 1, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, None, 0, None) == -1
     assert _status("act_quant", 0, FAKE, -1, 16, 16, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, None) == -2
-    assert _status("act_quant", 0, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 2, FAKE, 1 << 20, None) == -1
+    # unknown flags, and both given-flags at once
+    assert _status("act_quant", 0, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 4, FAKE, 1 << 20, None) == -1
+    assert _status("act_quant", 0, FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 3, FAKE, 1 << 20, None) == -1
+    # QA_AMAX_GIVEN reads amax from a 4-byte aligned workspace
+    assert _status("act_quant", 0, FAKE, 4, 16, 16, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000),
+                   ctypes.c_void_p(0x40000), 2, ctypes.c_void_p(0x50002), 1 << 20, None) == -3
     # q overlapping x
     assert _status("act_quant", 1, FAKE, 4, 16, 16, FAKE, ctypes.c_void_p(0x20000), None, 0,
                    None, 0, None) == -7
@@ -231,3 +236,19 @@ def test_step_control_validation():
     assert _status("qa_decide_step", None, *ok[1:], 4, 4, *st) == -1
     assert _status("qa_decide_step", *ok, 4, 4, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == -1
     assert _status("qa_decide_step", ctypes.c_void_p(FAKE.value + 4), *ok[1:], 4, 4, *st) == -3
+
+
+def test_amax_output_validation():
+    # the |max| output needs a target, 4-byte alignment and the staged bf16
+    # epilogue (16-byte aligned y, ldy % 4 == 0); it may not alias y or ws
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    y = ctypes.c_void_p(0x900000)
+    assert _status("qlinear_nvfp4_amax", *ok, 4, 4, 16, None, y, 4, 0, None, FAKE, 1 << 20, None) == -1
+    assert _status("qlinear_nvfp4_amax", *ok, 4, 4, 16, None, y, 4, 0, ctypes.c_void_p(0xA00002),
+                   FAKE, 1 << 20, None) == -3
+    assert _status("qlinear_nvfp4_amax", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900008), 4, 0,
+                   ctypes.c_void_p(0xA00000), FAKE, 1 << 20, None) == -4
+    assert _status("qlinear_int8_amax", *ok[:5], 4, 4, 16, None, y, 6, 0, ctypes.c_void_p(0xA00000),
+                   FAKE, 1 << 20, None) == -4
+    assert _status("qlinear_int8_amax", *ok[:5], 4, 4, 16, None, y, 4, 0, ctypes.c_void_p(0x900004),
+                   FAKE, 1 << 20, None) == -7

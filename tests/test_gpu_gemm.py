@@ -462,3 +462,77 @@ def test_quantized_output_saturating_scale():
     uc, us = _run_qout("nvfp4", a, wq, b, small, 64, 64, 64, False, fused=False)
     assert np.array_equal(codes, uc) and np.array_equal(scales, us)
     assert np.any(scales == 0x7E)              # E4M3 448 reached
+
+
+def _host_amax_bits(y_bits):
+    # float bits of max |bf16| over the stored outputs
+    return int((np.asarray(y_bits, np.uint16).astype(np.uint32) & 0x7FFF).max()) << 16
+
+
+# (M, N, K, bias+GELU): ragged rows and columns; bias and GELU; a K-split
+# shape (its fixup launch runs the epilogue)
+AMAX_SHAPES = [(300, 208, 256, False), (257, 528, 3088, True), (600, 704, 3840, False)]
+
+
+@pytest.mark.parametrize("M,N,K,bg", AMAX_SHAPES)
+@pytest.mark.parametrize("path", ["nvfp4", "int8"])
+def test_output_amax_and_amax_given_quant(M, N, K, bg, path):
+    # qlinear_*_amax stores the same bf16 output as qlinear_* and the |max|
+    # of it; act_quant NVFP4 with that amax given (QA_AMAX_GIVEN) gives the
+    # same codes, scales and tensor scale as act_quant's own amax pass
+    qa, t = _qa(), torch()
+    x, w = _case(M, N, K, seed=29)
+    wq = Q.nvfp4_encode(w)
+    w3 = (dev(wq[0]), dev(wq[1]), dev(np.array([wq[2]], np.float32)))
+    bias = dev(F.f64_to_bf16_rne(np.random.default_rng(3).normal(0, 0.5, N))) if bg else None
+    epi = qa.EPI_GELU_TANH if bg else qa.EPI_NONE
+    fmt = qa.NVFP4 if path == "nvfp4" else qa.INT8
+    ws = qa.workspace(qa.qlinear_workspace(fmt, M, N, K))
+    a = Q.nvfp4_encode(x) if path == "nvfp4" else Q.int8_encode(x)
+    qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, N))
+    qws[:4].zero_()
+    amax = qws[:4].view(t.int32)
+    y0 = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    y1 = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    if path == "nvfp4":
+        a3 = (dev(a[0]), dev(a[1]), dev(np.array([a[2]], np.float32)))
+        qa.qlinear_nvfp4(*a3, *w3, y0, M, N, K, bias=bias, epi=epi, ws=ws)
+        qa.qlinear_nvfp4_amax(*a3, *w3, y1, amax, M, N, K, bias=bias, epi=epi, ws=ws)
+    else:
+        a2 = (dev(a[0]), dev(a[1]))
+        qa.qlinear_int8(*a2, *w3, y0, M, N, K, bias=bias, epi=epi, ws=ws)
+        qa.qlinear_int8_amax(*a2, *w3, y1, amax, M, N, K, bias=bias, epi=epi, ws=ws)
+    t.cuda.synchronize()
+    yb = host(y1)
+    np.testing.assert_array_equal(yb, host(y0))
+    assert int(host(amax.view(t.int32))[0]) & 0xFFFFFFFF == _host_amax_bits(yb)
+    # the consumer's quantization with the produced amax
+    c0, s0, ts0 = qa.empty_nvfp4(M, N)
+    c1, s1, ts1 = qa.empty_nvfp4(M, N)
+    qa.act_quant(qa.NVFP4, y0.view(t.int16), c0, s0, ts0, 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, N)))
+    qa.act_quant(qa.NVFP4, y1.view(t.int16), c1, s1, ts1, qa.AMAX_GIVEN, qws)
+    t.cuda.synchronize()
+    for u, v in ((c0, c1), (s0, s1), (ts0, ts1)):
+        np.testing.assert_array_equal(host(u), host(v))
+    # and the oracle's encoding of the same bf16 output
+    oc, osc, ots = Q.nvfp4_encode(yb)
+    np.testing.assert_array_equal(host(c1), oc)
+    np.testing.assert_array_equal(host(s1), osc)
+    assert host(ts1)[0] == ots
+
+
+def test_output_amax_combines_with_preset():
+    # the word is max-combined: a larger preset value stays
+    qa, t = _qa(), torch()
+    M, N, K = 64, 64, 64
+    x, w = _case(M, N, K, seed=30)
+    a, wq = Q.int8_encode(x), Q.nvfp4_encode(w)
+    y = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    big = np.array([np.float32(1e30).view(np.int32)], np.int32)
+    amax = dev(big)
+    qa.qlinear_int8_amax(dev(a[0]), dev(a[1]), dev(wq[0]), dev(wq[1]),
+                         dev(np.array([wq[2]], np.float32)), y, amax, M, N, K,
+                         ws=qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K)))
+    t.cuda.synchronize()
+    assert host(amax)[0] == big[0]
