@@ -166,9 +166,17 @@ enum {
   kEpiQuant = 2,
   kEpiStagedBias = 3,
   kEpiStagedGelu = 4,
-  kEpiStagedBiasGelu = 5
+  kEpiStagedBiasGelu = 5,
+  // the staged kinds plus the |max| of the stored outputs: kind + kEpiAmax
+  kEpiAmax = 6
 };
-__host__ __device__ constexpr bool epi_staged(int k) { return k == kEpiPlain || k >= kEpiStagedBias; }
+__host__ __device__ constexpr bool epi_amax(int k) { return k >= kEpiAmax; }
+__host__ __device__ constexpr int epi_base(int k) {
+  return k < kEpiAmax ? k : (k == kEpiAmax ? kEpiPlain : k - kEpiAmax);
+}
+__host__ __device__ constexpr bool epi_staged(int k) {
+  return epi_base(k) == kEpiPlain || epi_base(k) >= kEpiStagedBias;
+}
 
 // ---------------------------------------------------------------- GEMM --
 
@@ -661,8 +669,9 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
     // bf16 staged per 32-row slice through this wave's own 8 KB of the idle
     // ring -- rows of 256 bytes, 16-byte chunk k of row r at slot k ^ (r &
     // 15) -- and stored as 4 rows x 256 contiguous bytes per instruction
-    constexpr bool kBias = kEpi == kEpiStagedBias || kEpi == kEpiStagedBiasGelu;
-    constexpr bool kGelu = kEpi == kEpiStagedGelu || kEpi == kEpiStagedBiasGelu;
+    constexpr int kB = epi_base(kEpi);
+    constexpr bool kBias = kB == kEpiStagedBias || kB == kEpiStagedBiasGelu;
+    constexpr bool kGelu = kB == kEpiStagedGelu || kB == kEpiStagedBiasGelu;
     uint8_t* const stg = smem + wave * 8192 * kPassTiles;
     uint32_t amx = 0;        // |max| of this lane's stored values (bf16 patterns)
     // bias of the lane's 64 columns (columns past N read column N-1)
@@ -720,12 +729,12 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
           uint16_t* yp = ybase + (int64_t)r * e.ldy + k * 8;
           if (k * 8 + 8 <= cols_left) {
             *reinterpret_cast<u32x4*>(yp) = d[it];
-            if (e.amax) amx = max(amx, fold_max(abs_max8_pk(d[it], u16x2{0, 0})));
+            if constexpr (epi_amax(kEpi)) amx = max(amx, fold_max(abs_max8_pk(d[it], u16x2{0, 0})));
           } else {
             for (int t = 0; k * 8 + t < cols_left; ++t) {
               const uint32_t b = (d[it][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
               yp[t] = (uint16_t)b;
-              amx = max(amx, b & 0x7FFFu);
+              if constexpr (epi_amax(kEpi)) amx = max(amx, b & 0x7FFFu);
             }
           }
         }
@@ -733,7 +742,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       // the next pass overwrites the slice after these reads (in order)
       asm volatile("" ::: "memory");
     }
-    if (e.amax) {
+    if constexpr (epi_amax(kEpi)) {
       // |bf16| patterns of the stored values order as the values do: the
       // wave's integer maximum, then one atomic maximum per wave of its
       // float bits (pattern << 16), as the act_quant amax pass reads them
@@ -993,8 +1002,9 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
   if (e.yq)
     kind = kEpiQuant;
   else if (!e.out_f32 && e.vec_ok)
-    kind = e.bias ? (e.gelu ? kEpiStagedBiasGelu : kEpiStagedBias)
-                  : (e.gelu ? kEpiStagedGelu : kEpiPlain);
+    kind = (e.bias ? (e.gelu ? kEpiStagedBiasGelu : kEpiStagedBias)
+                   : (e.gelu ? kEpiStagedGelu : kEpiPlain)) +
+           (e.amax ? kEpiAmax : 0);
   auto go = [&](auto i8c) {
     constexpr bool I8 = decltype(i8c)::value;
     switch (kind) {
@@ -1002,6 +1012,12 @@ static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipS
       case kEpiStagedBias: launch_one<I8, kEpiStagedBias>(grid, g, e, st); break;
       case kEpiStagedGelu: launch_one<I8, kEpiStagedGelu>(grid, g, e, st); break;
       case kEpiStagedBiasGelu: launch_one<I8, kEpiStagedBiasGelu>(grid, g, e, st); break;
+      case kEpiAmax + kEpiPlain: launch_one<I8, kEpiAmax + kEpiPlain>(grid, g, e, st); break;
+      case kEpiAmax + kEpiStagedBias: launch_one<I8, kEpiAmax + kEpiStagedBias>(grid, g, e, st); break;
+      case kEpiAmax + kEpiStagedGelu: launch_one<I8, kEpiAmax + kEpiStagedGelu>(grid, g, e, st); break;
+      case kEpiAmax + kEpiStagedBiasGelu:
+        launch_one<I8, kEpiAmax + kEpiStagedBiasGelu>(grid, g, e, st);
+        break;
       case kEpiQuant: launch_one<I8, kEpiQuant>(grid, g, e, st); break;
       default: launch_one<I8, kEpiGeneral>(grid, g, e, st); break;
     }
