@@ -339,19 +339,46 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     beta = np.full(L * J, 0.01, np.float32)
     i16 = lambda t: t.view(torch.int16)
 
-    def linear(fmt, x, ldx, lay, y, gelu, stream=stream):
+    # the hidden activation's NVFP4 quantization takes its tensor amax from
+    # the up projection's epilogue (word 0 of hws; bit-identical codes)
+    hws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
+    hamax = hws[:4].view(torch.int32)
+    lay_up = [None, None]
+
+    def linear(fmt, x, ldx, lay, y, gelu, stream=stream, amax_out=None, amax_ws=None):
         q, sc, ts, N, K = lay
         xv = torch.as_strided(x, (M, K), (ldx, 1))
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         if fmt == 0:
             aq = a4[0].view(-1)[: M * K // 2].view(M, K // 2)
             asc = a4[1].view(-1)[: M * K // 16].view(M, K // 16)
-            qa.act_quant(qa.NVFP4, i16(xv), aq, asc, a4[2], 0, qws, M=M, K=K, ldx=ldx, stream=stream)
-            qa.qlinear_nvfp4(aq, asc, a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+            if amax_ws is not None:
+                qa.act_quant(qa.NVFP4, i16(xv), aq, asc, a4[2], qa.AMAX_GIVEN, amax_ws, M=M, K=K,
+                             ldx=ldx, stream=stream)
+            else:
+                qa.act_quant(qa.NVFP4, i16(xv), aq, asc, a4[2], 0, qws, M=M, K=K, ldx=ldx,
+                             stream=stream)
+            if amax_out is not None:
+                qa.qlinear_nvfp4_amax(aq, asc, a4[2], q, sc, ts, y, amax_out, M, N, K, epi=epi,
+                                      ws=gws, stream=stream)
+            else:
+                qa.qlinear_nvfp4(aq, asc, a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=gws,
+                                 stream=stream)
         else:
             aq = a8[0].view(-1)[: M * K].view(M, K)
             qa.act_quant(qa.INT8, i16(xv), aq, a8[1], M=M, K=K, ldx=ldx, stream=stream)
-            qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+            if amax_out is not None:
+                qa.qlinear_int8_amax(aq, a8[1], q, sc, ts, y, amax_out, M, N, K, epi=epi, ws=gws,
+                                     stream=stream)
+            else:
+                qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+
+    def ffn_pair(fu, fd, stream=stream):
+        """up (GELU) and down projections; the up GEMM also produces the
+        hidden activation's |max| for an NVFP4 down projection."""
+        hamax.zero_()
+        linear(fu, x1, H, lay_up[0], u, True, stream=stream, amax_out=hamax)
+        linear(fd, u, F_, lay_up[1], dd, False, stream=stream, amax_ws=hws)
 
     # the drifting stack inputs x_t = bf16(x_{t-1} + 0.02 N(0,1)), made once
     xs = []
@@ -406,8 +433,8 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                     linear(m[0], cur, H, layers[l][0], qkv, False)
                     linear(m[1], qkv.view(-1)[2 * H:], 3 * H, layers[l][1], o, False)
                     qa.tdc_apply(i16(cur), i16(o), i16(x1), stream=stream)
-                    linear(m[2], x1, H, layers[l][2], u, True)
-                    linear(m[3], u, F_, layers[l][3], dd, False)
+                    lay_up[:] = layers[l][2:4]
+                    ffn_pair(m[2], m[3])
                     qa.tdc_apply(i16(x1), i16(dd), i16(out), stream=stream)
                     prev = ring[l][last[l]] if n_stored[l] else None
                     nxt = last[l] ^ 1
@@ -471,10 +498,11 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             for b in (sums, t_ctr, bstate, d_dev):
                 b.zero_()
 
-        def gated_linear(j, l, x, ldx, y, gelu, stream):
+        def gated_linear(j, l, x, ldx, y, gelu, stream, amax_out=None, amax_ws=None):
             for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
                 with qa.gate(lin[l * J + j:], bit):
-                    linear(fmt, x, ldx, layers[l][j], y, gelu, stream=stream)
+                    linear(fmt, x, ldx, layers[l][j], y, gelu, stream=stream, amax_out=amax_out,
+                           amax_ws=amax_ws)
 
         def step(stream):
             qa.decide_step(sums, alpha_d, beta_d, tau, delta, L, J, t_ctr, bstate, d_dev, blk,
@@ -490,8 +518,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                 gated_linear(1, l, qkv.view(-1)[2 * H:], 3 * H, o, False, stream)
                 with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
                     qa.tdc_apply(i16(cur), i16(o), i16(x1), stream=stream)
-                gated_linear(2, l, x1, H, u, True, stream)
-                gated_linear(3, l, u, F_, dd, False, stream)
+                hamax.zero_()             # (torch's fill kernel: runs in skipped blocks too)
+                gated_linear(2, l, x1, H, u, True, stream, amax_out=hamax)
+                gated_linear(3, l, u, F_, dd, False, stream, amax_ws=hws)
                 with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
                     qa.tdc_apply(i16(x1), i16(dd), i16(out), stream=stream)
                 for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
