@@ -68,9 +68,10 @@ typedef enum { QA_EPI_NONE = 0, QA_EPI_GELU_TANH = 1 } qa_epi;
 /* NVFP4 only: *tscale is an input (a calibrated or producer-computed s_T)
  * and the tensor amax pass is skipped. */
 #define QA_TSCALE_GIVEN 1u
-/* NVFP4 only: the tensor |max| amax_T is already in the first 4 bytes of
- * ws (float bits, as qlinear_nvfp4_amax / qlinear_int8_amax produce it);
- * the amax pass is skipped and s_T = amax_T / 2688 is computed from it and
+/* NVFP4 only: the tensor |max| amax_T is already in ws, as the 1024
+ * partial maxima (float bits) that qlinear_nvfp4_amax, qlinear_int8_amax
+ * or tdc_apply_amax leave there (the whole act_quant workspace, 4 KB); the
+ * amax pass is skipped, amax_T is their maximum and s_T = amax_T / 2688 is
  * written to *tscale -- the same s_T, bit for bit, as without the flag. */
 #define QA_AMAX_GIVEN 2u
 
@@ -167,13 +168,14 @@ int qlinear_int8(const int8_t* a_q, const float* a_s,
 /* qlinear_nvfp4_amax / qlinear_int8_amax: qlinear_nvfp4 / qlinear_int8
  * with a bf16 output (16-byte aligned, ldy % 4 == 0; otherwise
  * QA_EUNSUPPORTED) whose |max| over the stored values is also taken in the
- * GEMM epilogue and atomically max-combined into the device word *y_amax
- * (float bits; the caller sets it to 0 before the call).  Point y_amax at
- * the workspace of the act_quant NVFP4 call that quantizes y for the next
- * linear and pass QA_AMAX_GIVEN there: that call then skips its read of the
+ * GEMM epilogue and atomically max-combined into the 1024 device words
+ * y_amax[0..1023] (float bits; workgroup b into word b % 1024, so that the
+ * atomics spread; the caller zero-fills the 4 KB before the call).  Point
+ * y_amax at the workspace of the act_quant NVFP4 call that quantizes y for
+ * the next linear and pass QA_AMAX_GIVEN there: that call then skips its read of the
  * whole tensor for amax_T (6Bit-Diffusion, Fig. 2 caption: the consumer's
  * activations are quantized per linear; the producer already holds every
- * value).  y_amax must not overlap y, the inputs or ws. */
+ * value).  y_amax[0..1023] must not overlap y, the inputs or ws. */
 int qlinear_nvfp4_amax(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                        const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M,
                        int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
@@ -222,6 +224,17 @@ int tdc_update(const uint16_t* in, const uint16_t* out, const uint16_t* delta_pr
                void* ws, size_t ws_bytes, hipStream_t stream);
 int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
               double* sums2, void* ws, size_t ws_bytes, hipStream_t stream);
+/* tdc_apply that also takes the |max| of its bf16 outputs (each wave's
+ * integer maximum of the |bf16| patterns, one atomic maximum per wave of
+ * the float bits) into the 1024 device words out_amax[0..1023] (workgroup
+ * b into word b % 1024), which the caller zero-fills before the call: the
+ * tensor amax of the next linear's NVFP4 act_quant with QA_AMAX_GIVEN when
+ * out_amax is that call's workspace (the block input or the
+ * residual-added hidden state feeds the next linear).  out_amax: 4-byte
+ * aligned, its 4 KB overlapping no other buffer. */
+int tdc_apply_amax(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
+                   double* sums2, uint32_t* out_amax, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
 
 /* rel_err (Fig. 3 caption: E_rel, the layer-wise relative quantization
  * error at a timestep, to which the DMPQ predictor is fitted; read here as

@@ -55,6 +55,7 @@ _SIGS = {
     "block_gamma": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_update": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_apply": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "tdc_apply_amax": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "rel_err": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "delta_cosine": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_decide_cos": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
@@ -227,6 +228,14 @@ def tdc_apply(x_in, delta, x_out, sums2=None, ws=None, n=None, stream=None):
     n = x_in.numel() if n is None else n
     _check("tdc_apply", lib().tdc_apply(_ptr(x_in), _ptr(delta), _ptr(x_out), n, _ptr(sums2),
                                         _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def tdc_apply_amax(x_in, delta, x_out, out_amax, sums2=None, ws=None, n=None, stream=None):
+    """tdc_apply that also max-combines |x_out| into the device word out_amax."""
+    n = x_in.numel() if n is None else n
+    _check("tdc_apply_amax", lib().tdc_apply_amax(_ptr(x_in), _ptr(delta), _ptr(x_out), n,
+                                                  _ptr(sums2), _ptr(out_amax), _ptr(ws),
+                                                  _nbytes(ws), _stream(stream)))
 
 
 def rel_err(y_q, y_ref, sums2, ws, n=None, stream=None):

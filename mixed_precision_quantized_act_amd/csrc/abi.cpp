@@ -182,7 +182,8 @@ static int check_amax_out(const GemmOut& o, const uint32_t* y_amax, const void* 
   if (!y_amax) return QA_EINVAL;
   if (reinterpret_cast<uintptr_t>(y_amax) & 3u) return QA_EALIGN;
   if (!gemm_out_staged(o)) return QA_EUNSUPPORTED;
-  if (overlap(y, ybytes, y_amax, 4) || overlap(ws, ws_bytes, y_amax, 4)) return QA_EALIAS;
+  if (overlap(y, ybytes, y_amax, kAmaxSlots * 4) || overlap(ws, ws_bytes, y_amax, kAmaxSlots * 4))
+    return QA_EALIAS;
   return QA_OK;
 }
 
@@ -368,6 +369,24 @@ int tdc_apply(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t 
   if (overlap(out, b, delta, b)) return QA_EALIAS;
   if (out != in && overlap(out, b, in, b)) return QA_EALIAS;
   return hip_status(launch_tdc(2, in, delta, nullptr, out, n, sums2, ws, stream));
+}
+
+int tdc_apply_amax(const uint16_t* in, const uint16_t* delta, uint16_t* out, int64_t n,
+                   double* sums2, uint32_t* out_amax, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (!out || !out_amax) return QA_EINVAL;
+  if (int s = check_stream(in, delta, n, ws, ws_bytes, sums2 != nullptr)) return s;
+  if (!aligned16(out)) return QA_EALIGN;
+  if (reinterpret_cast<uintptr_t>(out_amax) & 3u) return QA_EALIGN;
+  const size_t b = (size_t)n * 2;
+  if (overlap(out, b, delta, b)) return QA_EALIAS;
+  if (out != in && overlap(out, b, in, b)) return QA_EALIAS;
+  const size_t ab = kAmaxSlots * 4;
+  if (overlap(out_amax, ab, out, b) || overlap(out_amax, ab, in, b) ||
+      overlap(out_amax, ab, delta, b) || overlap(out_amax, ab, ws, ws_bytes) ||
+      (sums2 && overlap(out_amax, ab, sums2, 16)))
+    return QA_EALIAS;
+  return hip_status(launch_tdc(5, in, delta, nullptr, out, n, sums2, ws, stream, out_amax));
 }
 
 int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2, void* ws,

@@ -209,7 +209,9 @@ int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t
 // ----------------------------------------------------------------- host --
 
 static constexpr int kAmaxBlocks = 1024;
-static_assert(kAmaxBlocks <= kPartsMax, "encoder folds at most kPartsMax partial maxima");
+static_assert(kAmaxBlocks <= kPartsMax && kAmaxSlots <= kPartsMax,
+              "encoder folds at most kPartsMax partial maxima");
+static_assert(kAmaxSlots <= kAmaxBlocks, "the workspace holds the producer's slots");
 // encoder: vectors in flight per lane, and at most this many workgroups
 // (one resident round; measured against 2 vectors per lane and an uncapped
 // grid, which pay the s_T fold again in every later workgroup)
@@ -223,7 +225,7 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
                               bool amax_given, void* ws, hipStream_t stream) {
   const Gate gt = current_gate();
   float* partial = static_cast<float*>(ws);
-  int nblk = 1;                  // amax_given: the one partial maximum is ws[0]
+  int nblk = kAmaxSlots;         // amax_given: the producer's partial maxima in ws
   if (!given && !amax_given) {
     const bool contig = ldx == K;
     const int64_t work = contig ? (M * K / 8 + 256 * kUnroll - 1) / (256 * kUnroll) : M;

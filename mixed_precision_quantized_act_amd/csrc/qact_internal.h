@@ -16,6 +16,13 @@ struct Gate {
 };
 Gate current_gate();
 
+// A producer-computed tensor amax (qlinear_*_amax, tdc_apply_amax) is kept
+// as kAmaxSlots partial maxima (float bits, non-negative: they order as
+// integers), workgroup b max-combining into slot b % kAmaxSlots so that the
+// atomics spread over many addresses; act_quant's workspace holds exactly
+// these slots, and QA_AMAX_GIVEN folds them as it folds its own amax pass.
+constexpr int kAmaxSlots = 1024;
+
 // Gate bits written by the device-side decisions (launch_decide): per
 // linear, which activation format runs (none when its block is skipped);
 // per block, the compute path with ring slot `last` = 0 or 1 (the Delta
@@ -75,8 +82,10 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 size_t reduce_ws_bytes(int64_t n);
-// mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine
+// mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine,
+// 5: tdc_apply that also max-combines |out| into *amax_out
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* delta_prev,
-                      uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream);
+                      uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream,
+                      uint32_t* amax_out = nullptr);
 
 }  // namespace qact

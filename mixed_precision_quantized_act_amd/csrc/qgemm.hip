@@ -748,7 +748,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       // float bits (pattern << 16), as the act_quant amax pass reads them
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, o, 64));
-      if (lane == 0) atomicMax(e.amax, amx << 16);
+      if (lane == 0) atomicMax(e.amax + (blockIdx.x % kAmaxSlots), amx << 16);
     }
   } else if constexpr (kEpi == kEpiQuant) {
     // NVFP4 output with the given tensor scale s_T: every output is rounded

@@ -33,7 +33,10 @@ static constexpr int kThreads = 256;
 static constexpr int kUnroll = QACT_TDC_UNROLL;
 static_assert(kRedBlocks % kThreads == 0, "finalize loads kRedBlocks / kThreads rows per thread");
 
-enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3, MODE_COS = 4 };
+// MODE_APPLY_AMAX: tdc_apply that also max-combines the |max| of its
+// bf16 outputs into a device word (the consumer's NVFP4 tensor amax)
+enum { MODE_GAMMA = 0, MODE_UPDATE = 1, MODE_APPLY = 2, MODE_RELERR = 3, MODE_COS = 4,
+       MODE_APPLY_AMAX = 5 };
 
 struct Acc4 {
   double s[4];
@@ -60,7 +63,7 @@ __device__ __forceinline__ uint32_t tdc_pair(uint32_t xi, uint32_t bi, uint32_t 
     a.s[1] = __fma_rn((double)b, (double)b, a.s[1]);
     return 0;
   }
-  if (MODE == MODE_APPLY) {
+  if (MODE == MODE_APPLY || MODE == MODE_APPLY_AMAX) {
     const uint32_t o = f32_to_bf16(x + b);
     const double od = (double)__uint_as_float(o << 16);
     a.s[0] += fabs(od - (double)x);
@@ -86,8 +89,12 @@ template <int MODE, bool PREV>
 __global__ void __launch_bounds__(kThreads)
 tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
            const uint16_t* __restrict__ prev, uint16_t* dst, int64_t n,
-           double* __restrict__ partial, int want_sums, Gate gate) {
+           double* __restrict__ partial, int want_sums, uint32_t* __restrict__ amax_out,
+           Gate gate) {
   if (gated_off(gate)) return;
+  constexpr bool kAmax = MODE == MODE_APPLY_AMAX;
+  constexpr bool kWrites = MODE == MODE_UPDATE || MODE == MODE_APPLY || kAmax;
+  uint32_t amx = 0;            // |max| of this thread's outputs (bf16 patterns)
   Acc4 a = {{0.0, 0.0, 0.0, 0.0}};
   const int64_t nvec = n / 8;
   // kUnroll vectors per thread and sweep: all loads issued before any use
@@ -117,8 +124,10 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
         const uint32_t hi = tdc_pair<MODE, PREV>(xv[u][i] >> 16, bv[u][i] >> 16, pv[u][i] >> 16, a);
         ov[i] = lo | (hi << 16);
       }
-      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && MODE != MODE_COS && v < nvec)
+      if (kWrites && v < nvec) {
         __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst) + v);
+        if constexpr (kAmax) amx = max(amx, fold_max(abs_max8_pk(ov, u16x2{0, 0})));
+      }
     }
   }
   // ragged tail (n % 8 elements), done by workgroup 0
@@ -126,8 +135,15 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
     const int64_t e = nvec * 8 + threadIdx.x;
     if (e < n) {
       const uint32_t o = tdc_pair<MODE, PREV>(in[e], b[e], PREV ? prev[e] : 0u, a);
-      if (MODE != MODE_GAMMA && MODE != MODE_RELERR && MODE != MODE_COS) dst[e] = (uint16_t)o;
+      if (kWrites) dst[e] = (uint16_t)o;
+      if constexpr (kAmax) amx = max(amx, o & 0x7FFFu);
     }
+  }
+  if constexpr (kAmax) {
+    // the wave's integer maximum, one atomic maximum per wave (float bits)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, o, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(amax_out + (blockIdx.x % kAmaxSlots), amx << 16);
   }
   if (!want_sums) return;
   __shared__ double red[4][kThreads / 64];
@@ -249,7 +265,8 @@ hipError_t launch_decide(const double* sums, const float* alpha, const float* be
 size_t reduce_ws_bytes(int64_t) { return (size_t)kRedBlocks * 4 * sizeof(double); }
 
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* prev,
-                      uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream) {
+                      uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream,
+                      uint32_t* amax_out) {
   const Gate gt = current_gate();
   const int64_t nvec = n / 8;
   int64_t nb = (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll);
@@ -260,22 +277,25 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   const dim3 g((unsigned)nb), t(kThreads);
   if (mode == MODE_GAMMA)
     hipLaunchKernelGGL((tdc_kernel<MODE_GAMMA, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
+                       partial, want, amax_out, gt);
   else if (mode == MODE_UPDATE && prev)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, true>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
+                       partial, want, amax_out, gt);
   else if (mode == MODE_UPDATE)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
+                       partial, want, amax_out, gt);
   else if (mode == MODE_APPLY)
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
+                       partial, want, amax_out, gt);
   else if (mode == MODE_RELERR)
     hipLaunchKernelGGL((tdc_kernel<MODE_RELERR, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
-  else
+                       partial, want, amax_out, gt);
+  else if (mode == MODE_COS)
     hipLaunchKernelGGL((tdc_kernel<MODE_COS, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, gt);
+                       partial, want, amax_out, gt);
+  else
+    hipLaunchKernelGGL((tdc_kernel<MODE_APPLY_AMAX, false>), g, t, 0, stream, in, b, prev, dst,
+                       n, partial, want, amax_out, gt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !want) return e;
   const int ncols = mode == MODE_UPDATE ? 4 : mode == MODE_COS ? 3 : 2;

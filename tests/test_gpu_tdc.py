@@ -225,3 +225,43 @@ def test_delta_cosine_worked_example():
     got = gpu_cosine(e1, v)
     assert list(got) == [3.0, 1.0, 25.0]
     assert _qa().cosine_from_sums(got) == 0.6
+
+
+def test_tdc_apply_amax_feeds_nvfp4_quant():
+    # tdc_apply_amax writes the same output and sums as tdc_apply and the
+    # |max| of the output; act_quant NVFP4 with that amax (QA_AMAX_GIVEN)
+    # equals act_quant's own amax pass and the oracle's encoding
+    import mixed_precision_quantized_act_amd as qa
+    from oracle import quant as Q
+    t = torch()
+    M, H = 777, 1920                      # a ragged element count per vector sweep
+    x = synth.activations(4, M, H, "normal")
+    d = synth.gamma_pair(4, x, 0.05)
+    delta = T.tdc_update(x.ravel(), d.ravel())[0].reshape(M, H)
+    xd, dd = dev(x).view(-1), dev(delta).view(-1)
+    rws = qa.workspace(qa.reduce_workspace(M * H))
+    o0 = t.empty(M * H, dtype=t.int16, device="cuda")
+    o1 = t.empty(M * H, dtype=t.int16, device="cuda")
+    s0 = t.zeros(2, dtype=t.float64, device="cuda")
+    s1 = t.zeros(2, dtype=t.float64, device="cuda")
+    qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, H))
+    qws.zero_()
+    qa.tdc_apply(xd, dd, o0, s0, rws)
+    qa.tdc_apply_amax(xd, dd, o1, qws[:4096].view(t.int32), s1, rws)
+    t.cuda.synchronize()
+    ob = host(o1).view(np.uint16)
+    np.testing.assert_array_equal(ob, host(o0).view(np.uint16))
+    np.testing.assert_array_equal(host(s1), host(s0))
+    want = int((ob.astype(np.uint32) & 0x7FFF).max()) << 16
+    assert int(host(qws[:4096].view(t.int32)).astype(np.int64).max()) == want
+    c0, sc0, ts0 = qa.empty_nvfp4(M, H)
+    c1, sc1, ts1 = qa.empty_nvfp4(M, H)
+    qa.act_quant(qa.NVFP4, o0.view(M, H), c0, sc0, ts0, 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, H)))
+    qa.act_quant(qa.NVFP4, o1.view(M, H), c1, sc1, ts1, qa.AMAX_GIVEN, qws)
+    t.cuda.synchronize()
+    for u, v in ((c0, c1), (sc0, sc1), (ts0, ts1)):
+        np.testing.assert_array_equal(host(u), host(v))
+    oc, osc, ots = Q.nvfp4_encode(ob.reshape(M, H))
+    np.testing.assert_array_equal(host(c1), oc)
+    assert host(ts1)[0] == ots
