@@ -125,7 +125,8 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
         ov[i] = lo | (hi << 16);
       }
       if (kWrites && v < nvec) {
-        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst) + v);
+        // plain stores: nontemporal ones measured 5-8 % slower here
+        reinterpret_cast<u32x4*>(dst)[v] = ov;
         if constexpr (kAmax) amx = max(amx, fold_max(abs_max8_pk(ov, u16x2{0, 0})));
       }
     }
@@ -270,7 +271,9 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   const Gate gt = current_gate();
   const int64_t nvec = n / 8;
   int64_t nb = (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  if (nb > kRedBlocks) nb = kRedBlocks;
+  // with sums, at most kRedBlocks partial rows; without, one sweep (measured
+  // faster for tdc_apply: 37.0 -> 35.4 us at 17776 x 1920)
+  if (nb > (sums ? kRedBlocks : 65535)) nb = sums ? kRedBlocks : 65535;
   if (nb < 1) nb = 1;
   double* partial = static_cast<double*>(ws);
   const int want = sums != nullptr;
