@@ -36,8 +36,12 @@
  *   - work is enqueued on ``stream`` and the call returns without waiting;
  *     device faults surface at the caller's next synchronisation;
  *   - vector buffers must be 16-byte aligned; row strides are in elements;
- *   - results are deterministic: no floating-point atomics anywhere;
- *   - calls on different streams must not share output or scratch buffers.
+ *   - results are deterministic: no floating-point atomics anywhere (the
+ *     producer-side tensor amax uses integer atomic maxima, whose result
+ *     does not depend on their order);
+ *   - calls on different streams must not share output or scratch buffers;
+ *   - a gate set with qa_set_gate applies to every later call of the same
+ *     host thread until cleared.
  */
 #ifndef QACT_H
 #define QACT_H
