@@ -337,3 +337,38 @@ def test_decide_step_against_oracle_rules():
         computed = skip == 0
         sums.copy_(t.from_numpy(sums_seq[step]))
     assert int(host(t_ctr)[0]) == steps
+
+
+def test_gate_closed_k_split_nvfp4_and_amax_calls():
+    # a closed gate also stops the NVFP4 GEMM's scale re-layout, the K-split
+    # slice and fixup launches, the amax epilogue and tdc_apply_amax
+    qa, t = _qa(), torch()
+    M, N, K = 600, 704, 3840                       # 9 tiles split in 4 slices
+    x = dev(synth.activations(3, M, K, "normal"))
+    w = dev(synth.activations(4, N, K, "normal"))
+    wq, ws, wts = qa.empty_nvfp4(N, K)
+    aq, asc, ats = qa.empty_nvfp4(M, K)
+    qw = qa.workspace(qa.act_quant_workspace(qa.NVFP4, max(M, N), K))
+    qa.act_quant(qa.NVFP4, w, wq, ws, wts, 0, qw)
+    qa.act_quant(qa.NVFP4, x, aq, asc, ats, 0, qw)
+    flag = t.zeros(1, dtype=t.uint8, device="cuda")
+    gws = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, N, K))
+    y = t.full((M, N), -7.0, dtype=t.bfloat16, device="cuda")
+    amax = t.full((1024,), 5, dtype=t.int32, device="cuda")
+    d = t.full((M * N,), 0x5A5A, dtype=t.int16, device="cuda")
+    am2 = t.full((1024,), 5, dtype=t.int32, device="cuda")
+    with qa.gate(flag, 1):
+        qa.qlinear_nvfp4(aq, asc, ats, wq, ws, wts, y, M, N, K, ws=gws)
+        qa.qlinear_nvfp4_amax(aq, asc, ats, wq, ws, wts, y, amax, M, N, K, ws=gws)
+        yv = y.view(t.int16).view(-1)
+        qa.tdc_apply_amax(yv, yv, d, am2)
+    t.cuda.synchronize()
+    assert (host(y).view(np.uint16) == np.uint16(0xC0E0)).all()      # bf16 -7.0
+    assert (host(amax) == 5).all() and (host(am2) == 5).all()
+    assert (host(d).view(np.uint16) == 0x5A5A).all()
+    # and open, the same calls run
+    flag.fill_(1)
+    with qa.gate(flag, 1):
+        qa.qlinear_nvfp4(aq, asc, ats, wq, ws, wts, y, M, N, K, ws=gws)
+    t.cuda.synchronize()
+    assert not (host(y).view(np.uint16) == np.uint16(0xC0E0)).all()
