@@ -339,10 +339,17 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     beta = np.full(L * J, 0.01, np.float32)
     i16 = lambda t: t.view(torch.int16)
 
-    # the hidden activation's NVFP4 quantization takes its tensor amax from
-    # the up projection's epilogue (the partial-maximum slots of hws; bit-identical codes)
-    hws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
-    hamax = hws[:4096].view(torch.int32)             # the 1024 partial-maximum slots
+    # Every NVFP4 activation takes its tensor amax from its producer (bit-
+    # identical codes): slots[l] holds block l's three 1024-word partial-
+    # maximum arrays -- [0] its input (from block l-1's output add), [1] x1
+    # (from the residual add), [2] the hidden activation (from the up
+    # GEMM's epilogue) -- all zeroed by one fill at the start of a step;
+    # block 0's input has no producer.  Each array doubles as the consumer
+    # act_quant's 4 KB workspace.
+    slots = torch.zeros((L + 1, 3, 1024), dtype=torch.int32, device=dev)
+    assert qa.act_quant_workspace(qa.NVFP4, M, F_) == 4096
+    sl_w = lambda l, k: slots[l, k]                       # int32 words (producer side)
+    sl_ws = lambda l, k: slots[l, k].view(torch.uint8)    # the same 4 KB (consumer ws)
     lay_up = [None, None]
 
     def linear(fmt, x, ldx, lay, y, gelu, stream=stream, amax_out=None, amax_ws=None):
@@ -373,24 +380,17 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             else:
                 qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
 
-    def ffn_pair(fu, fd, stream=stream):
-        """up (GELU) and down projections; the up GEMM also produces the
-        hidden activation's |max| for an NVFP4 down projection, and the
-        up projection's NVFP4 input takes x1's |max| from the residual add."""
-        hamax.zero_()
-        linear(fu, x1, H, lay_up[0], u, True, stream=stream, amax_out=hamax, amax_ws=x1ws)
-        linear(fd, u, F_, lay_up[1], dd, False, stream=stream, amax_ws=hws)
-
-    # the block inputs' and x1's tensor amax from the residual adds
-    # (tdc_apply_amax): block l reads inws[l % 2] (from block l - 1's output)
-    # and produces inws[(l + 1) % 2]; block 0's input has no producer
-    inws = [qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, H), dev) for _ in range(2)]
-    x1ws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, H), dev)
-    word = lambda w: w[:4096].view(torch.int32)      # the 1024 partial-maximum slots
+    def ffn_pair(l, fu, fd, stream=stream):
+        """up (GELU) and down projections of block l; the up GEMM also
+        produces the hidden activation's |max| for an NVFP4 down projection,
+        and the up projection's NVFP4 input takes x1's |max| from the
+        residual add."""
+        linear(fu, x1, H, lay_up[0], u, True, stream=stream, amax_out=sl_w(l, 2),
+               amax_ws=sl_ws(l, 1))
+        linear(fd, u, F_, lay_up[1], dd, False, stream=stream, amax_ws=sl_ws(l, 2))
 
     def apply_amax(a, b, out, target, sums2=None, stream=stream):
-        word(target).zero_()
-        qa.tdc_apply_amax(i16(a), i16(b), i16(out), word(target), sums2, rws, stream=stream)
+        qa.tdc_apply_amax(i16(a), i16(b), i16(out), target, sums2, rws, stream=stream)
 
     # the drifting stack inputs x_t = bf16(x_{t-1} + 0.02 N(0,1)), made once
     xs = []
@@ -433,21 +433,22 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             else:
                 skip = qa.tdc_decide(t, d_prev, computed_prev, delta)
             cur = xd
+            slots.zero_()                 # one fill for every producer's amax slots
             for l in range(L):
                 out = torch.empty_like(cur)
                 if skip[l]:
-                    apply_amax(cur, ring[l][last[l]], out, inws[(l + 1) % 2], sums[l, :2])
+                    apply_amax(cur, ring[l][last[l]], out, sl_w(l + 1, 0), sums[l, :2])
                     computed_prev[l] = 0
                     skipped += 1
                 else:
                     m = mask[l * J:(l + 1) * J]
                     linear(m[0], cur, H, layers[l][0], qkv, False,
-                           amax_ws=inws[l % 2] if l else None)
+                           amax_ws=sl_ws(l, 0) if l else None)
                     linear(m[1], qkv.view(-1)[2 * H:], 3 * H, layers[l][1], o, False)
-                    apply_amax(cur, o, x1, x1ws)
+                    apply_amax(cur, o, x1, sl_w(l, 1))
                     lay_up[:] = layers[l][2:4]
-                    ffn_pair(m[2], m[3])
-                    apply_amax(x1, dd, out, inws[(l + 1) % 2])
+                    ffn_pair(l, m[2], m[3])
+                    apply_amax(x1, dd, out, sl_w(l + 1, 0))
                     prev = ring[l][last[l]] if n_stored[l] else None
                     nxt = last[l] ^ 1
                     qa.tdc_update(i16(cur), i16(out), None if prev is None else i16(prev),
@@ -519,28 +520,26 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
         def step(stream):
             qa.decide_step(sums, alpha_d, beta_d, tau, delta, L, J, t_ctr, bstate, d_dev, blk,
                            lin, None, skip_o, stream=stream)
+            slots.zero_()                 # (on the capturing stream when captured)
             cur = x_in
             for l in range(L):
                 out = outs[l]
                 r0, r1 = ring[l]
-                nxt_in = inws[(l + 1) % 2]
-                word(nxt_in).zero_()      # (torch's fill kernels run in every case)
                 for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
                     with qa.gate(blk[l:], bit):
-                        qa.tdc_apply_amax(i16(cur), i16(slot), i16(out), word(nxt_in),
+                        qa.tdc_apply_amax(i16(cur), i16(slot), i16(out), sl_w(l + 1, 0),
                                           sums[l, :2], rws, stream=stream)
                 gated_linear(0, l, cur, H, qkv, False, stream,
-                             amax_ws=inws[l % 2] if l else None)
+                             amax_ws=sl_ws(l, 0) if l else None)
                 gated_linear(1, l, qkv.view(-1)[2 * H:], 3 * H, o, False, stream)
-                word(x1ws).zero_()
                 with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
-                    qa.tdc_apply_amax(i16(cur), i16(o), i16(x1), word(x1ws), None, rws,
+                    qa.tdc_apply_amax(i16(cur), i16(o), i16(x1), sl_w(l, 1), None, rws,
                                       stream=stream)
-                hamax.zero_()
-                gated_linear(2, l, x1, H, u, True, stream, amax_out=hamax, amax_ws=x1ws)
-                gated_linear(3, l, u, F_, dd, False, stream, amax_ws=hws)
+                gated_linear(2, l, x1, H, u, True, stream, amax_out=sl_w(l, 2),
+                             amax_ws=sl_ws(l, 1))
+                gated_linear(3, l, u, F_, dd, False, stream, amax_ws=sl_ws(l, 2))
                 with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
-                    qa.tdc_apply_amax(i16(x1), i16(dd), i16(out), word(nxt_in), None, rws,
+                    qa.tdc_apply_amax(i16(x1), i16(dd), i16(out), sl_w(l + 1, 0), None, rws,
                                       stream=stream)
                 for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
                     with qa.gate(blk[l:], bit):
