@@ -96,7 +96,8 @@ const char* qa_build_info(void);
  * tscale NVFP4: f32 device scalar, output (or input with QA_TSCALE_GIVEN);
  *        QA_AMAX_GIVEN takes amax_T from ws (see above), needs ws 4-aligned;
  *        INT8: must be NULL
- * M >= 0 (M == 0 enqueues nothing), 0 < K, K % 16 == 0 for NVFP4.
+ * 0 <= M < 2^26 (M == 0 enqueues nothing), 0 < K < 2^23, K % 16 == 0 for
+ * NVFP4 (QA_ESHAPE otherwise).
  * ------------------------------------------------------------------------ */
 size_t act_quant_workspace(qa_fmt fmt, int64_t M, int64_t K);
 int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -124,8 +125,8 @@ int qlinear_nvfp4_q(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                     const float* y_ts, uint8_t* y_q, uint8_t* y_s, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
-                   const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
-                   const uint16_t* bias, qa_epi epi, const float* y_ts, uint8_t* y_q,
+                   const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M, int64_t N,
+                   int64_t K, const uint16_t* bias, qa_epi epi, const float* y_ts, uint8_t* y_q,
                    uint8_t* y_s, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -137,13 +138,18 @@ int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
  * W NVFP4 [N][K] (w_q, w_s, w_ts).  bias: bf16 [N] or NULL.
  * y: bf16 or f32 [M][ldy], ldy >= N.  epi: QA_EPI_GELU_TANH applies
  * 0.5 v (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3))) after the bias.
- * Accuracy: both paths multiply exactly dequantized operands (each NVFP4
- * value E2M1 x E4M3 and each int8 is exact in fp16; the tensor scales and
- * the INT8 row scales are applied to the float32 sums), so an output
- * differs from the exact (float64) product by the float32 accumulation
- * over K -- about K 2^-24 times sum_k |a_k w_k| at worst -- plus the final
- * rounding to the output type; the relative Frobenius error is far below
- * 1e-3.
+ * INT8 activations with w8 (the weight's digit planes from
+ * int8_weight_planes, below): integer MFMA, exact int32 sums H and L per
+ * output (see qlinear_int8_acc), Y = s_a[m] s_Tw 2^(X[n]-1) (256 H + L)
+ * formed in float32 (three roundings); w_q and w_s are then not read and
+ * may be NULL.  Without w8 (NULL), and always for NVFP4 activations, both
+ * operands are expanded exactly to fp16 (each NVFP4 value E2M1 x E4M3 and
+ * each int8 is exact in fp16) and multiplied on fp16 MFMA with float32
+ * accumulation, the tensor scales and the INT8 row scales applied to the
+ * sums: an output then differs from the exact (float64) product by the
+ * float32 accumulation over K -- about K 2^-24 times sum_k |a_k w_k| at
+ * worst -- plus the final rounding to the output type.  Either way the
+ * relative Frobenius error is far below 1e-3.
  * Workspace: qlinear_workspace() bytes, device memory that the call may
  * overwrite: a per-tile copy of the E4M3 scales of the operands (about
  * (M + N) K / 16 bytes) and, for shapes whose last round of 256 x 256
@@ -154,8 +160,11 @@ int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
  * split (summed in another order: equal within the accuracy above).  When
  * K is a multiple of 64 and w_s is 4-byte aligned the INT8 call reads the
  * weight scales in place and needs no more workspace than the split's (it
- * may then be NULL, and runs unsplit).
- * y must not overlap any input.  Requires 0 < K, K % 16 == 0, M, N >= 0.
+ * may then be NULL, and runs unsplit).  With w8 the INT8 call needs no
+ * scale copies; its K split keeps int32 partial sums (256 KB per slice).
+ * y must not overlap any input.  Requires 0 < K < 2^23, K % 16 == 0,
+ * 0 <= M, N < 2^26 (QA_ESHAPE otherwise: the kernels address a tile's
+ * 256 operand rows with 32-bit offsets below 2^31).
  * ------------------------------------------------------------------------ */
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
 int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
@@ -164,10 +173,42 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                   void* y, int64_t ldy, qa_out out, qa_epi epi,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 int qlinear_int8(const int8_t* a_q, const float* a_s,
-                 const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                 const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, const void* w8,
                  int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                  void* y, int64_t ldy, qa_out out, qa_epi epi,
                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * INT8 path on integer MFMA.  6Bit-Diffusion, abstract: volatile layers
+ * keep INT8 activations; Table 2 ("W4A6"): the weights stay 4-bit NVFP4.
+ *
+ * int8_weight_planes (set-up, once per weight; SYNCHRONISES `stream`):
+ * writes into w8 (device, int8_weight_planes_bytes(N, K) bytes, 256-byte
+ * aligned, owned by the caller and passed to the INT8 linears) the NVFP4
+ * weight (w_q, w_s) [N][K] in integer form.  An E4M3 scale is c 2^x (normal
+ * codes: c = 8 + mantissa, x = exponent field - 10; subnormal: c =
+ * mantissa, x = -9) and an E2M1 value v/2 (v in 0, 1, 2, 3, 4, 6, 8, 12,
+ * signed); with X[n] the smallest x over row n's non-zero scales,
+ * W[n][k] = s_Tw 2^(X[n]-1) I[n][k], I = v c 2^(x - X[n]), and
+ * I = 256 hi + lo with int8 digits lo in [-128, 127], |hi| <= 90.  This
+ * holds for rows whose x spread (largest minus smallest) is at most 7;
+ * other rows are "irregular": their count goes to *irregular_rows (host,
+ * nullable) and the call returns QA_EUNSUPPORTED (the buffer must then
+ * not be used; the linear runs without w8).  The tensor scale is not
+ * part of w8 (w_ts is passed to each linear).
+ *
+ * qlinear_int8_acc (verification): the exact int32 sums of the linear,
+ * acc_hi[m][n] = H = sum_k q[m][k] hi[n][k] and acc_lo = L = sum_k
+ * q[m][k] lo[n][k] (int32 device arrays [M][N]) from the same integer
+ * MFMA kernel.  Requires K < 2^17 (|H|, |L| < 2^31).  acc_hi and acc_lo
+ * must not overlap each other or the inputs.
+ * ------------------------------------------------------------------------ */
+size_t int8_weight_planes_bytes(int64_t N, int64_t K);
+int int8_weight_planes(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                       void* w8, size_t w8_bytes, int64_t* irregular_rows,
+                       hipStream_t stream);
+int qlinear_int8_acc(const int8_t* a_q, const void* w8, int64_t M, int64_t N, int64_t K,
+                     int32_t* acc_hi, int32_t* acc_lo, hipStream_t stream);
 
 /* qlinear_nvfp4_amax / qlinear_int8_amax: qlinear_nvfp4 / qlinear_int8
  * with a bf16 output (16-byte aligned, ldy % 4 == 0; otherwise
@@ -186,16 +227,18 @@ int qlinear_nvfp4_amax(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts
                        qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
-                      const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
-                      const uint16_t* bias, void* y, int64_t ldy, qa_epi epi, uint32_t* y_amax,
-                      void* ws, size_t ws_bytes, hipStream_t stream);
+                      const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                      int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
+                      qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 /* act_quant of x followed by the matching qlinear_* (one layer).  For
  * NVFP4 the tensor scale is computed from x (flags may hold
- * QA_TSCALE_GIVEN with *x_ts an input); for INT8 x_ts is unused. */
+ * QA_TSCALE_GIVEN with *x_ts an input); for INT8 x_ts is unused and w8
+ * (nullable) selects the integer-MFMA kernel; for NVFP4 w8 must be NULL. */
 size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
 int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t flags,
-            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, const void* w8,
             int64_t M, int64_t N, int64_t K, const uint16_t* bias,
             void* y, int64_t ldy, qa_out out, qa_epi epi,
             void* ws, size_t ws_bytes, hipStream_t stream);

@@ -38,19 +38,22 @@ _SIGS = {
     "qlinear_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "qlinear_nvfp4": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                      ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
-    "qlinear_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
+    "qlinear_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                     ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
+    "int8_weight_planes_bytes": (_SZ, [_I64, _I64]),
+    "int8_weight_planes": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _SZ, _P, _P]),
+    "qlinear_int8_acc": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P]),
     "qlinear_nvfp4_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int,
                                        _P, _P, _P, _P, _SZ, _P]),
-    "qlinear_int8_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _P,
-                                      _P, _P, _P, _SZ, _P]),
+    "qlinear_int8_q": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int,
+                                      _P, _P, _P, _P, _SZ, _P]),
     "qlinear_nvfp4_amax": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                           ctypes.c_int, _P, _P, _SZ, _P]),
-    "qlinear_int8_amax": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
+    "qlinear_int8_amax": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                          ctypes.c_int, _P, _P, _SZ, _P]),
     "qlinear_layer_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
-    "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _I64, _I64,
-                               _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
+    "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _P, _I64,
+                               _I64, _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
     "reduce_workspace": (_SZ, [_I64]),
     "block_gamma": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_update": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -151,11 +154,43 @@ def qlinear_nvfp4(a_q, a_s, a_ts, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT
 
 
 def qlinear_int8(a_q, a_s, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, epi=EPI_NONE,
-                 ws=None, ldy=None, stream=None):
+                 ws=None, ldy=None, stream=None, w8=None):
+    """INT8 linear; w8 (the weight's digit planes) selects the integer-MFMA kernel."""
     ldy = y.stride(0) if ldy is None else ldy
     _check("qlinear_int8", lib().qlinear_int8(
-        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), _ptr(y),
-        ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias),
+        _ptr(y), ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def int8_weight_planes_bytes(N, K):
+    return lib().int8_weight_planes_bytes(N, K)
+
+
+def int8_weight_planes(w_q, w_s, w8, N, K, stream=None):
+    """Write the NVFP4 weight's int8 digit planes into w8 (device, set-up;
+    synchronises the stream).  Returns the number of irregular rows (0 on
+    success); raises QactError (QA_EUNSUPPORTED) when some row is irregular."""
+    import ctypes as _c
+    cnt = _c.c_int64(0)
+    st = lib().int8_weight_planes(_ptr(w_q), _ptr(w_s), N, K, _ptr(w8), _nbytes(w8),
+                                  _c.addressof(cnt), _stream(stream))
+    _check("int8_weight_planes", st)
+    return cnt.value
+
+
+def int8_weight_planes_count(w_q, w_s, w8, N, K, stream=None):
+    """As int8_weight_planes, but returns (status, irregular rows) instead of raising."""
+    import ctypes as _c
+    cnt = _c.c_int64(0)
+    st = lib().int8_weight_planes(_ptr(w_q), _ptr(w_s), N, K, _ptr(w8), _nbytes(w8),
+                                  _c.addressof(cnt), _stream(stream))
+    return st, cnt.value
+
+
+def qlinear_int8_acc(a_q, w8, acc_hi, acc_lo, M, N, K, stream=None):
+    """The INT8 linear's exact int32 sums H (hi plane) and L (lo plane), [M, N] each."""
+    _check("qlinear_int8_acc", lib().qlinear_int8_acc(
+        _ptr(a_q), _ptr(w8), M, N, K, _ptr(acc_hi), _ptr(acc_lo), _stream(stream)))
 
 
 def qlinear_nvfp4_q(a_q, a_s, a_ts, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bias=None,
@@ -167,11 +202,11 @@ def qlinear_nvfp4_q(a_q, a_s, a_ts, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bia
 
 
 def qlinear_int8_q(a_q, a_s, w_q, w_s, w_ts, y_ts, y_q, y_s, M, N, K, bias=None, epi=EPI_NONE,
-                   ws=None, stream=None):
+                   ws=None, stream=None, w8=None):
     """INT8 linear with the output quantized to NVFP4 (given tensor scale y_ts)."""
     _check("qlinear_int8_q", lib().qlinear_int8_q(
-        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), epi,
-        _ptr(y_ts), _ptr(y_q), _ptr(y_s), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias),
+        epi, _ptr(y_ts), _ptr(y_q), _ptr(y_s), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def qlinear_nvfp4_amax(a_q, a_s, a_ts, w_q, w_s, w_ts, y, y_amax, M, N, K, bias=None,
@@ -184,12 +219,12 @@ def qlinear_nvfp4_amax(a_q, a_s, a_ts, w_q, w_s, w_ts, y, y_amax, M, N, K, bias=
 
 
 def qlinear_int8_amax(a_q, a_s, w_q, w_s, w_ts, y, y_amax, M, N, K, bias=None, epi=EPI_NONE,
-                      ws=None, ldy=None, stream=None):
+                      ws=None, ldy=None, stream=None, w8=None):
     """qlinear_int8 (bf16 out) that also max-combines |y| into y_amax."""
     ldy = y.stride(0) if ldy is None else ldy
     _check("qlinear_int8_amax", lib().qlinear_int8_amax(
-        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K, _ptr(bias), _ptr(y), ldy,
-        epi, _ptr(y_amax), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias),
+        _ptr(y), ldy, epi, _ptr(y_amax), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def qlinear_layer_workspace(fmt, M, N, K):
@@ -197,12 +232,12 @@ def qlinear_layer_workspace(fmt, M, N, K):
 
 
 def qlinear(fmt, x, x_ts, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, epi=EPI_NONE,
-            flags=0, ws=None, ldx=None, ldy=None, stream=None):
+            flags=0, ws=None, ldx=None, ldy=None, stream=None, w8=None):
     ldx = x.stride(0) if ldx is None else ldx
     ldy = y.stride(0) if ldy is None else ldy
     _check("qlinear", lib().qlinear(
-        fmt, _ptr(x), ldx, _ptr(x_ts), flags, _ptr(w_q), _ptr(w_s), _ptr(w_ts), M, N, K,
-        _ptr(bias), _ptr(y), ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
+        fmt, _ptr(x), ldx, _ptr(x_ts), flags, _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N,
+        K, _ptr(bias), _ptr(y), ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ------------------------------------------------------------- Gamma / TDC --

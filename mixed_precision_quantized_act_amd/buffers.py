@@ -25,3 +25,14 @@ def empty_int8_act(rows, K, device="cuda"):
     torch = _torch()
     return (torch.empty((rows, K), dtype=torch.int8, device=device),
             torch.empty((rows,), dtype=torch.float32, device=device))
+
+
+def empty_int8_planes(N, K, device="cuda"):
+    """Device buffer for an NVFP4 weight's int8 digit planes
+    (int8_weight_planes), 256-byte aligned."""
+    from ._lib import int8_weight_planes_bytes
+    torch = _torch()
+    nbytes = int8_weight_planes_bytes(N, K)
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]

@@ -16,7 +16,14 @@ using namespace qact;
 
 namespace {
 
-constexpr int64_t kMaxDim = (int64_t)1 << 31;   // rows / columns / K limit
+// Size limits.  The GEMM kernels address a tile's operand rows (at most 256
+// rows of at most K bytes) with 32-bit buffer offsets and mark a load to be
+// skipped with an offset just below 2^31, so 256 K must stay below 2^31;
+// one workgroup of 256 threads per tile or per 4 activation rows keeps every
+// grid below 2^32 threads.
+constexpr int64_t kMaxRows = (int64_t)1 << 26;  // M, N
+constexpr int64_t kMaxK = (int64_t)1 << 23;
+constexpr int64_t kMaxTiles = (int64_t)1 << 24; // 256 x 128 output tiles of one linear
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -30,8 +37,17 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 int hip_status(hipError_t e) { return e == hipSuccess ? QA_OK : QA_EHIP; }
 
 int check_mk(int64_t M, int64_t K) {
-  if (M < 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim) return QA_ESHAPE;
+  if (M < 0 || K <= 0 || M >= kMaxRows || K >= kMaxK) return QA_ESHAPE;
   if (K % 16) return QA_ESHAPE;
+  return QA_OK;
+}
+
+// a linear's N and its tile count; the NVFP4 call's per-tile scale copy
+// is one workgroup per (256-row tile, K unit of 64) of both operands
+int check_nk(int64_t M, int64_t N, int64_t K) {
+  if (N < 0 || N >= kMaxRows) return QA_ESHAPE;
+  if (((M + 255) / 256) * ((N + 127) / 128) > kMaxTiles) return QA_ESHAPE;
+  if (((M + 255) / 256 + (N + 255) / 256) * ((K + 63) / 64) > kMaxTiles) return QA_ESHAPE;
   return QA_OK;
 }
 
@@ -58,7 +74,7 @@ const char* qa_strerror(int status) {
   switch (status) {
     case QA_OK: return "ok";
     case QA_EINVAL: return "invalid argument (null pointer, bad enum or negative size)";
-    case QA_ESHAPE: return "bad shape (K must be a positive multiple of 16; ld >= K; sizes < 2^31)";
+    case QA_ESHAPE: return "bad shape (K must be a positive multiple of 16 below 2^23; ld >= K; rows below 2^26)";
     case QA_EALIGN: return "misaligned buffer (16-byte alignment required)";
     case QA_EUNSUPPORTED: return "unsupported combination";
     case QA_EWORKSPACE: return "workspace too small";
@@ -114,15 +130,22 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
 
 // -------------------------------------------------------------- qlinear --
 
+// the INT8 linear takes the integer-MFMA kernel when given w8 and the fp16
+// kernel otherwise: its workspace covers either
+static size_t int8_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t a = int8_gemm_ws_bytes(M, N, K), b = int8_i8_gemm_ws_bytes(M, N, K);
+  return a > b ? a : b;
+}
+
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K <= 0) return 0;
-  return fmt == QA_NVFP4 ? nvfp4_gemm_ws_bytes(M, N, K) : int8_gemm_ws_bytes(M, N, K);
+  return fmt == QA_NVFP4 ? nvfp4_gemm_ws_bytes(M, N, K) : int8_ws_bytes(M, N, K);
 }
 
 static int check_linear(int64_t M, int64_t N, int64_t K, const void* y, int64_t ldy,
                         qa_out out, qa_epi epi) {
   if (int s = check_mk(M, K)) return s;
-  if (N < 0 || N >= kMaxDim) return QA_ESHAPE;
+  if (int s = check_nk(M, N, K)) return s;
   if (int s = check_out(out, epi)) return s;
   if (!y) return QA_EINVAL;
   if (ldy < N) return QA_ESHAPE;
@@ -152,27 +175,99 @@ int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
   return hip_status(launch_nvfp4_gemm(a_q, a_s, a_ts, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
 }
 
+// the INT8 linear's weight operands: the digit planes w8 (integer MFMA;
+// w_q and w_s unused) or the NVFP4 weight itself (fp16 MFMA)
+static int check_int8_weight(const uint8_t* w_q, const uint8_t* w_s, const void* w8) {
+  if (w8) return (reinterpret_cast<uintptr_t>(w8) & 255u) ? QA_EALIGN : QA_OK;
+  if (!w_q || !w_s) return QA_EINVAL;
+  return aligned16(w_q) ? QA_OK : QA_EALIGN;
+}
+static size_t int8_ws_need(int64_t M, int64_t N, int64_t K, const uint8_t* w_s, const void* w8) {
+  return w8 ? 0 : int8_gemm_ws_need(M, N, K, w_s);
+}
+static size_t int8_weight_bytes(int64_t N, int64_t K, const void* w8) {
+  return w8 ? int8_planes_bytes(N, K) : (size_t)(N * K / 2);
+}
+static hipError_t launch_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                              const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                              int64_t N, int64_t K, const GemmOut& o, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (w8)
+    return launch_int8_i8_gemm(a_q, a_s, w8, w_ts, M, N, K, o, ws, ws_bytes, nullptr, nullptr,
+                               stream);
+  return launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream);
+}
+
 int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
-                 const float* w_ts, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
-                 void* y, int64_t ldy, qa_out out, qa_epi epi, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
-  if (!a_q || !a_s || !w_q || !w_s || !w_ts) return QA_EINVAL;
+                 const float* w_ts, const void* w8, int64_t M, int64_t N, int64_t K,
+                 const uint16_t* bias, void* y, int64_t ldy, qa_out out, qa_epi epi, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !a_s || !w_ts) return QA_EINVAL;
+  if (int s = check_int8_weight(w_q, w_s, w8)) return s;
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
-  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  if (!aligned16(a_q)) return QA_EALIGN;
   {
-    const size_t need = int8_gemm_ws_need(M, N, K, w_s);
+    const size_t need = int8_ws_need(M, N, K, w_s, w8);
     if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
   }
   if (!aligned16(ws)) return QA_EALIGN;
   const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * (out == QA_OUT_F32 ? 4 : 2) : 0;
-  if (overlap(y, ybytes, a_q, (size_t)(M * K)) || overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
+  if (overlap(y, ybytes, a_q, (size_t)(M * K)) ||
+      overlap(y, ybytes, w8 ? w8 : w_q, int8_weight_bytes(N, K, w8)) ||
       overlap(y, ybytes, ws, ws_bytes))
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {y, ldy, out == QA_OUT_F32, epi == QA_EPI_GELU_TANH, bias};
   o.y_amax = g_out_amax;
-  return hip_status(
-      launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
+  return hip_status(launch_int8(a_q, a_s, w_q, w_s, w_ts, w8, M, N, K, o, ws, ws_bytes, stream));
+}
+
+size_t int8_weight_planes_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % 16) return 0;
+  return int8_planes_bytes(N, K);
+}
+
+int int8_weight_planes(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K, void* w8,
+                       size_t w8_bytes, int64_t* irregular_rows, hipStream_t stream) {
+  if (!w_q || !w_s || !w8) return QA_EINVAL;
+  if (int s = check_mk(N, K)) return s;
+  if (reinterpret_cast<uintptr_t>(w8) & 255u) return QA_EALIGN;
+  if (w8_bytes < int8_planes_bytes(N, K)) return QA_EWORKSPACE;
+  if (overlap(w8, w8_bytes, w_q, (size_t)(N * K / 2)) || overlap(w8, w8_bytes, w_s, (size_t)(N * K / 16)))
+    return QA_EALIAS;
+  if (irregular_rows) *irregular_rows = 0;
+  if (N == 0) return QA_OK;
+  int* cnt = int8_planes_counter(w8, N, K);
+  if (hipMemsetAsync(cnt, 0, sizeof(int), stream) != hipSuccess) return QA_EHIP;
+  if (launch_int8_planes(w_q, w_s, N, K, w8, cnt, stream) != hipSuccess) return QA_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, cnt, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return QA_EHIP;
+  if (irregular_rows) *irregular_rows = host;
+  return host ? QA_EUNSUPPORTED : QA_OK;
+}
+
+int qlinear_int8_acc(const int8_t* a_q, const void* w8, int64_t M, int64_t N, int64_t K,
+                     int32_t* acc_hi, int32_t* acc_lo, hipStream_t stream) {
+  if (!a_q || !w8 || !acc_hi || !acc_lo) return QA_EINVAL;
+  if (int s = check_mk(M, K)) return s;
+  if (int s = check_nk(M, N, K)) return s;
+  if (K >= ((int64_t)1 << 17)) return QA_ESHAPE;
+  if (!aligned16(a_q)) return QA_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(w8) & 255u) || (reinterpret_cast<uintptr_t>(acc_hi) & 3u) ||
+      (reinterpret_cast<uintptr_t>(acc_lo) & 3u))
+    return QA_EALIGN;
+  const size_t ab = (size_t)(M * N) * 4;
+  if (overlap(acc_hi, ab, acc_lo, ab) || overlap(acc_hi, ab, a_q, (size_t)(M * K)) ||
+      overlap(acc_lo, ab, a_q, (size_t)(M * K)) ||
+      overlap(acc_hi, ab, w8, int8_planes_bytes(N, K)) ||
+      overlap(acc_lo, ab, w8, int8_planes_bytes(N, K)))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  GemmOut o = {nullptr, N, 0, 0, nullptr};
+  return hip_status(launch_int8_i8_gemm(a_q, nullptr, w8, nullptr, M, N, K, o, nullptr, 0, acc_hi,
+                                        acc_lo, stream));
 }
 
 // bf16 output and its |max| (the tensor amax of a following NVFP4
@@ -206,9 +301,10 @@ int qlinear_nvfp4_amax(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts
 }
 
 int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
-                      const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N, int64_t K,
-                      const uint16_t* bias, void* y, int64_t ldy, qa_epi epi, uint32_t* y_amax,
-                      void* ws, size_t ws_bytes, hipStream_t stream) {
+                      const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                      int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
+                      qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
   GemmOut o = {y, ldy, 0, epi == QA_EPI_GELU_TANH, bias};
   o.y_amax = y_amax;
   if (y && ldy >= N && M > 0 && N > 0)
@@ -216,8 +312,8 @@ int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
       return s;
   if (!y_amax) return QA_EINVAL;
   g_out_amax = y_amax;
-  const int s = qlinear_int8(a_q, a_s, w_q, w_s, w_ts, M, N, K, bias, y, ldy, QA_OUT_BF16, epi,
-                             ws, ws_bytes, stream);
+  const int s = qlinear_int8(a_q, a_s, w_q, w_s, w_ts, w8, M, N, K, bias, y, ldy, QA_OUT_BF16,
+                             epi, ws, ws_bytes, stream);
   g_out_amax = nullptr;
   return s;
 }
@@ -227,7 +323,8 @@ int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
 static int check_qout(int64_t M, int64_t N, int64_t K, qa_epi epi, const float* y_ts,
                       const uint8_t* y_q, const uint8_t* y_s) {
   if (int s = check_mk(M, K)) return s;
-  if (N < 0 || N >= kMaxDim || N % 16) return QA_ESHAPE;
+  if (int s = check_nk(M, N, K)) return s;
+  if (N % 16) return QA_ESHAPE;
   if (int s = check_out(QA_OUT_BF16, epi)) return s;
   if (!y_ts || !y_q || !y_s) return QA_EINVAL;
   if (!aligned16(y_q)) return QA_EALIGN;
@@ -264,22 +361,24 @@ int qlinear_nvfp4_q(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
 }
 
 int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
-                   const float* w_ts, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
-                   qa_epi epi, const float* y_ts, uint8_t* y_q, uint8_t* y_s, void* ws,
-                   size_t ws_bytes, hipStream_t stream) {
-  if (!a_q || !a_s || !w_q || !w_s || !w_ts) return QA_EINVAL;
+                   const float* w_ts, const void* w8, int64_t M, int64_t N, int64_t K,
+                   const uint16_t* bias, qa_epi epi, const float* y_ts, uint8_t* y_q,
+                   uint8_t* y_s, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!a_q || !a_s || !w_ts) return QA_EINVAL;
+  if (int s = check_int8_weight(w_q, w_s, w8)) return s;
   if (int s = check_qout(M, N, K, epi, y_ts, y_q, y_s)) return s;
-  if (!aligned16(a_q) || !aligned16(w_q)) return QA_EALIGN;
+  if (!aligned16(a_q)) return QA_EALIGN;
   {
-    const size_t need = int8_gemm_ws_need(M, N, K, w_s);
+    const size_t need = int8_ws_need(M, N, K, w_s, w8);
     if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
   }
   if (!aligned16(ws)) return QA_EALIGN;
-  if (qout_aliases(y_q, y_s, M, N, a_q, (size_t)(M * K), w_q, (size_t)(N * K / 2), ws, ws_bytes))
+  if (qout_aliases(y_q, y_s, M, N, a_q, (size_t)(M * K), w8 ? w8 : w_q,
+                   int8_weight_bytes(N, K, w8), ws, ws_bytes))
     return QA_EALIAS;
   if (M == 0 || N == 0) return QA_OK;
   GemmOut o = {nullptr, N, 0, epi == QA_EPI_GELU_TANH, bias, y_q, y_s, y_ts};
-  return hip_status(launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream));
+  return hip_status(launch_int8(a_q, a_s, w_q, w_s, w_ts, w8, M, N, K, o, ws, ws_bytes, stream));
 }
 
 size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
@@ -287,14 +386,16 @@ size_t qlinear_layer_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
   if (fmt == QA_NVFP4)
     return round256((size_t)(M * K / 2)) + round256((size_t)(M * K / 16)) +
            round256(nvfp4_quant_ws_bytes(M, K)) + nvfp4_gemm_ws_bytes(M, N, K);
-  return round256((size_t)(M * K)) + round256((size_t)M * 4) + int8_gemm_ws_bytes(M, N, K);
+  return round256((size_t)(M * K)) + round256((size_t)M * 4) + int8_ws_bytes(M, N, K);
 }
 
 int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t flags,
-            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, int64_t M, int64_t N,
-            int64_t K, const uint16_t* bias, void* y, int64_t ldy, qa_out out, qa_epi epi,
-            void* ws, size_t ws_bytes, hipStream_t stream) {
+            const uint8_t* w_q, const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+            int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy, qa_out out,
+            qa_epi epi, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (fmt != QA_NVFP4 && fmt != QA_INT8) return QA_EINVAL;
+  if (fmt == QA_NVFP4 && w8) return QA_EINVAL;
+  if (int s = fmt == QA_INT8 ? check_int8_weight(w_q, w_s, w8) : QA_OK) return s;
   if (!x || !ws) return QA_EINVAL;
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (ws_bytes < qlinear_layer_workspace(fmt, M, N, K)) return QA_EWORKSPACE;
@@ -322,8 +423,8 @@ int qlinear(qa_fmt fmt, const uint16_t* x, int64_t ldx, float* x_ts, uint32_t fl
   p += round256((size_t)M * 4);
   int s = act_quant(QA_INT8, x, M, K, ldx, aq, as, nullptr, 0, nullptr, 0, stream);
   if (s) return s;
-  return qlinear_int8(aq, as, w_q, w_s, w_ts, M, N, K, bias, y, ldy, out, epi, p,
-                      int8_gemm_ws_bytes(M, N, K), stream);
+  return qlinear_int8(aq, as, w_q, w_s, w_ts, w8, M, N, K, bias, y, ldy, out, epi, p,
+                      int8_ws_bytes(M, N, K), stream);
 }
 
 // ---------------------------------------------------------------- Gamma --
@@ -408,6 +509,7 @@ int delta_cosine(const uint16_t* d_new, const uint16_t* d_prev, int64_t n, doubl
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
   set_gemm_events(before, after);
+  set_i8_gemm_events(before, after);
   return QA_OK;
 }
 

@@ -80,6 +80,21 @@ hipError_t launch_int8_gemm(const int8_t* a_q, const float* a_s, const uint8_t* 
                             int64_t K, const GemmOut& o, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+// ---- INT8 path on integer MFMA (qgemm_i8.hip): the NVFP4 weight as two
+// int8 digit planes made once at set-up, and the GEMM with exact int32 sums
+size_t int8_planes_bytes(int64_t N, int64_t K);
+// device int32 counter of the irregular rows inside the planes buffer
+int* int8_planes_counter(void* w8, int64_t N, int64_t K);
+hipError_t launch_int8_planes(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                              void* w8, int* irregular_dev, hipStream_t stream);
+size_t int8_i8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+// acc_hi/acc_lo non-null: store the int32 sums H and L [M][N] instead of y
+hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* w8,
+                               const float* w_ts, int64_t M, int64_t N, int64_t K,
+                               const GemmOut& o, void* ws, size_t ws_bytes, int32_t* acc_hi,
+                               int32_t* acc_lo, hipStream_t stream);
+void set_i8_gemm_events(hipEvent_t before, hipEvent_t after);
+
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 size_t reduce_ws_bytes(int64_t n);
 // mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine,

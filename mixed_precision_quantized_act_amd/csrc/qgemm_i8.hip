@@ -1,0 +1,586 @@
+// INT8-activation linear on gfx950 integer MFMA with exact int32 sums.
+//
+// 6Bit-Diffusion, abstract: volatile layers keep INT8 activations; Table 2
+// ("W4A6"): the weights stay 4-bit NVFP4.  The layer is
+//   Y[m][n] = s_a[m] s_Tw sum_k q[m][k] E4M3(sw[n][k/16]) E2M1(w[n][k]).
+//
+// Integer form of an NVFP4 weight row.  An E4M3 scale is c 2^x with an
+// integer significand c (normal codes: 8 + mantissa, x = exponent - 10;
+// subnormal codes: mantissa, x = -9) and an E2M1 value is v / 2 with
+// v in {0, 1, 2, 3, 4, 6, 8, 12} (with sign).  With X[n] the smallest x over
+// the row's non-zero scales,
+//   W[n][k] = s_Tw 2^(X[n] - 1) I[n][k],   I = v c 2^(x - X[n]),
+// an integer with |I| <= 180 2^spread (spread = largest minus smallest x of
+// the row).  For spread <= 7, |I| <= 23040 splits into two int8 digits,
+// I = 256 hi + lo with lo in [-128, 127] and |hi| <= 90, so that
+//   Y[m][n] = s_a[m] s_Tw 2^(X[n] - 1) (256 H[m][n] + L[m][n]),
+//   H = sum_k q hi,  L = sum_k q lo,
+// two exact int32 sums (|H|, |L| <= K 127 128 < 2^31 for K < 2^17) from
+// v_mfma_i32_32x32x32_i8.  The digit planes are made once per weight at
+// set-up (int8_planes_kernel) in the layout the GEMM loads: no conversion
+// of either operand in the GEMM's loop.  Rows with a wider spread are
+// reported at set-up; their linears take the exact-operand fp16 kernel.
+//
+// Workgroup: 4 waves (one per SIMD), 256 activation rows x 128 weight rows,
+// i.e. a 256 x 256 integer tile against the two planes.  Wave w owns
+// activation rows 64 w .. +64 and all 256 plane rows (2 x 8 MFMA tiles of
+// 32 x 32; tiles j < 4 take the lo plane, j >= 4 the hi plane of the same
+// 128 columns).  K runs in units of 64 (two MFMA k-steps of 32): per unit
+// the tile's 16 KB of activations and 16 KB of plane rows are DMA'd
+// (buffer_load ... lds) into a 4-slot LDS ring, three units ahead; each wave
+// reads its fragments straight from the ring, one unit ahead.
+#include <hip/hip_ext.h>
+
+#include "qgemm_common.h"
+
+namespace qact {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileM = 256;                     // activation rows per tile
+constexpr int kTileN = 128;                     // weight rows (output columns) per tile
+constexpr int kUnitK = 64;                      // K per unit (two k-steps of 32)
+constexpr int kSlots = 4;                       // LDS ring slots (units)
+constexpr int kUnitBytes = 256 * kUnitK;        // one operand's unit in LDS
+constexpr int kWOff = kUnitBytes + 128;         // plane rows after the activations
+constexpr int kSlot = 2 * kWOff;
+constexpr int kColF = kSlots * kSlot;           // the tile's 128 column factors (float)
+constexpr int kRowS = kColF + kTileN * 4;       // and its 256 row scales s_a s_Tw (float)
+constexpr int kSmem = kRowS + kTileM * 4;
+constexpr int kLoads = 8;                       // DMA instructions per wave per unit
+constexpr int kFM = 2, kFN = 8;                 // MFMA tiles per wave (rows, plane rows)
+constexpr int kSpreadMax = 7;                   // largest exponent spread of a row
+static_assert(kSmem <= 160 * 1024, "LDS");
+static_assert(kSmem >= 4 * 8192 * kPassTiles, "epilogue staging");
+
+// K split of the last round of tiles (as in the fp16 kernel): one
+// workgroup per CU, at most 4 slices, each at least 2 units, taken when it
+// takes at least kSplitMinSaved units off the last round (the fixup
+// launch reads 256 KB per slice and tile: it costs about as much as the
+// fp16 kernel's 15-20 units, i.e. 30-40 of these half-length units).
+constexpr int kCUs = 256;
+constexpr int kMaxSplits = 4;
+constexpr int kSplitMinSaved = 40;
+constexpr int kPartTile = 4 * 256 * 64;         // int32 partial sums of one tile
+
+inline int64_t units_of(int64_t K) { return (K + kUnitK - 1) / kUnitK; }
+inline int64_t ntiles_of(int64_t N) { return (N + kTileN - 1) / kTileN; }
+inline size_t r256(size_t v) { return (v + 255) / 256 * 256; }
+
+// LDS / packed-plane position of 16-byte chunk c (K bytes 16c .. 16c+15
+// of a unit) of row r: chunks are XOR-swizzled by bit 2 of the row so that
+// the 32 rows of a fragment read spread over the banks.
+__host__ __device__ constexpr int chunk_slot(int r, int c) { return c ^ (((r >> 2) & 1) * 2); }
+
+// E4M3 code -> (c, x) with value c 2^x.
+__device__ __forceinline__ void e4m3_sig_exp(uint32_t s, int& c, int& x) {
+  const int e = (int)((s >> 3) & 15u), m = (int)(s & 7u);
+  c = e ? 8 + m : m;
+  x = e ? e - 10 : -9;
+}
+
+}  // namespace
+
+// --------------------------------------------------------- weight planes --
+
+// Packed planes of an NVFP4 weight [N][K]: for weight-row tile t (128
+// rows) and unit u, 16 KB at ((t * units + u) * 16384): plane row
+// pr = plane * 128 + r (plane 0 = lo, 1 = hi) holds its 64 digits at
+// pr * 64, chunk c at slot chunk_slot(pr, c).  Rows past N and K past the
+// weight are zero.  Then float rowf[tiles * 128] = 2^(X[n] - 1) (0 for
+// all-zero, irregular and padding rows) and the int32 count of irregular
+// rows.  One wave per row; lane l takes element 64 u + l of each unit.
+__global__ void __launch_bounds__(256)
+int8_planes_kernel(const uint8_t* __restrict__ w_q, const uint8_t* __restrict__ w_s, int64_t N,
+                   int64_t K, int units, int8_t* __restrict__ planes, float* __restrict__ rowf,
+                   int* __restrict__ irregular) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // < tiles * 128
+  const int lane = threadIdx.x & 63;
+  const int64_t gpr = K / 16;
+  int xmin = 64, xmax = -64;
+  if (n < N)
+    for (int64_t gi = lane; gi < gpr; gi += 64) {
+      int c, x;
+      e4m3_sig_exp(w_s[n * gpr + gi], c, x);
+      if (c) {
+        xmin = min(xmin, x);
+        xmax = max(xmax, x);
+      }
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    xmin = min(xmin, __shfl_xor(xmin, o, 64));
+    xmax = max(xmax, __shfl_xor(xmax, o, 64));
+  }
+  const bool live = xmin <= xmax;                 // a non-zero scale exists
+  const bool regular = !live || xmax - xmin <= kSpreadMax;
+  if (lane == 0) {
+    rowf[n] = live && regular ? ldexpf(1.0f, xmin - 1) : 0.0f;
+    if (!regular) atomicAdd(irregular, 1);
+  }
+  const int r = (int)(n % kTileN);
+  int8_t* const tile = planes + (n / kTileN) * (int64_t)units * kUnitBytes;
+  for (int u = 0; u < units; ++u) {
+    const int64_t k = (int64_t)u * kUnitK + lane;
+    int I = 0;
+    if (live && regular && k < K) {
+      const uint32_t code = (w_q[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 15u;
+      int c, x;
+      e4m3_sig_exp(w_s[n * gpr + k / 16], c, x);
+      I = c ? e2m1_twice(code) * c * (1 << (x - xmin)) : 0;
+    }
+    const int lo = ((I + 128) & 255) - 128;
+    const int hi = (I - lo) / 256;
+    int8_t* const unit = tile + (int64_t)u * kUnitBytes;
+    const int c = lane >> 4, b = lane & 15;
+    unit[r * 64 + 16 * chunk_slot(r, c) + b] = (int8_t)lo;
+    unit[(kTileN + r) * 64 + 16 * chunk_slot(kTileN + r, c) + b] = (int8_t)hi;
+  }
+}
+
+size_t int8_planes_bytes(int64_t N, int64_t K) {
+  const int64_t t = ntiles_of(N);
+  return r256((size_t)(t * units_of(K)) * kUnitBytes) + r256((size_t)t * kTileN * 4) + 256;
+}
+
+hipError_t launch_int8_planes(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                              void* w8, int* irregular_dev, hipStream_t st) {
+  const int64_t t = ntiles_of(N);
+  int8_t* planes = static_cast<int8_t*>(w8);
+  float* rowf = reinterpret_cast<float*>(static_cast<uint8_t*>(w8) +
+                                         r256((size_t)(t * units_of(K)) * kUnitBytes));
+  hipLaunchKernelGGL(int8_planes_kernel, dim3((unsigned)(t * kTileN / 4)), dim3(256), 0, st, w_q,
+                     w_s, N, K, (int)units_of(K), planes, rowf, irregular_dev);
+  return hipGetLastError();
+}
+
+int* int8_planes_counter(void* w8, int64_t N, int64_t K) {
+  const int64_t t = ntiles_of(N);
+  return reinterpret_cast<int*>(static_cast<uint8_t*>(w8) +
+                                r256((size_t)(t * units_of(K)) * kUnitBytes) +
+                                r256((size_t)t * kTileN * 4));
+}
+
+// ------------------------------------------------------------------ GEMM --
+
+struct I8Args {
+  const uint8_t* a;          // int8 activations [M][K]
+  const int8_t* planes;      // packed weight planes
+  const float* rowf;         // 2^(X[n] - 1) per weight row
+  const float* a_rs;         // activation row scales s_a
+  const float* w_ts;         // weight tensor scale s_Tw
+  int64_t K;
+  int units;
+  int mt, nt;                // tile counts
+  int main_tiles, grid_main; // whole tiles and their grid (a multiple of 8)
+  int splits, split_units;   // K split of the tail tiles
+  int32_t* part;             // slice partial sums, kPartTile per (tail tile, slice)
+  int32_t* acc_hi;           // kEpiAcc: the sums H and L, int32 [M][N]
+  int32_t* acc_lo;
+  Gate gate;
+};
+
+// the test-only epilogue: store H and L themselves
+constexpr int kEpiAcc = 100;
+enum { kWhole = 0, kSlice = 1, kFixup = 2 };
+
+template <int kEpi, int kMode>
+__global__ void __launch_bounds__(kThreads, 1)
+qgemm_i8_kernel(I8Args g, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  if (gated_off(g.gate)) return;
+
+  // tile of this workgroup: XCD-aware order as in the fp16 kernel (each
+  // XCD a contiguous range of logical tiles, grouped 8 tile-rows at a time)
+  const int bid = (int)blockIdx.x;
+  int logical, slice = 0, u_begin = 0, u_count = g.units;
+  if constexpr (kMode == kWhole) {
+    const int per_xcd = (g.main_tiles + 7) / 8;
+    logical = (bid & 7) * per_xcd + (bid >> 3);
+    if (logical >= g.main_tiles) return;
+  } else if constexpr (kMode == kSlice) {
+    logical = g.main_tiles + bid / g.splits;
+    slice = bid % g.splits;
+    u_begin = slice * g.split_units;
+    u_count = min(g.units - u_begin, g.split_units);
+  } else {
+    logical = g.main_tiles + bid;
+  }
+  constexpr int kGroup = 8;
+  const int group = logical / (kGroup * g.nt);
+  const int first_m = group * kGroup;
+  const int gsz = min(g.mt - first_m, kGroup);
+  const int in_group = logical - group * kGroup * g.nt;
+  const int tm = first_m + in_group % gsz;
+  const int tn = in_group / gsz;
+  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = g.K;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  i32x16 acc[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  // epilogue factors, read now so that their latency hides under the loop
+  // and kept in LDS (written once the loop has started; a loop barrier
+  // makes them visible): the tile's 128 column factors 2^(X[n] - 1) (the
+  // array is padded to whole tiles) and its 256 row scales s_a s_Tw (rows
+  // past M read row M-1; they are never stored)
+  constexpr bool kFactors = kEpi != kEpiAcc && kMode != kSlice;
+  const int64_t wave_row0 = m0 + 64 * wave;
+  float cfv = 0.0f, rsv = 0.0f;
+  float* const colf = reinterpret_cast<float*>(smem + kColF);
+  float* const rows = reinterpret_cast<float*>(smem + kRowS);
+  auto put_factors = [&] {
+    if (tid < kTileN) colf[tid] = cfv;
+    rows[tid] = rsv;
+  };
+  if constexpr (kFactors) {
+    rsv = g.a_rs[min<int64_t>(m0 + tid, e.M - 1)] * *g.w_ts;
+    if (tid < kTileN) cfv = g.rowf[n0 + tid];
+    if constexpr (kMode == kFixup) {
+      put_factors();
+      __syncthreads();
+    }
+  }
+
+  if constexpr (kMode != kFixup) {
+    // Activations: rows m0 .. (at most 256), K bytes from the slice start;
+    // rows past M fall outside the buffer and load zero, as do chunks past
+    // K (passed the out-of-range offset).  Planes: the tile's units from the
+    // slice start, always in range (padded at set-up).
+    const int64_t a_rows = min<int64_t>(e.M - m0, kTileM);
+    const uint32_t a_skip = (uint32_t)u_begin * kUnitK;
+    const uint32_t a_lim = (uint32_t)K - a_skip;
+    const __amdgpu_buffer_rsrc_t ra =
+        buffer_rsrc(g.a + m0 * K + a_skip, (uint32_t)(a_rows * K) - a_skip);
+    const __amdgpu_buffer_rsrc_t rw =
+        buffer_rsrc(g.planes + ((int64_t)tn * g.units + u_begin) * kUnitBytes,
+                    (uint32_t)u_count * (uint32_t)kUnitBytes);
+    constexpr uint32_t kOOB = 0x7FFFFFF0u;
+
+    // DMA of unit u into slot u % kSlots.  One instruction fills 1 KB of
+    // LDS: 16 activation rows (lane l: row l/4, LDS slot l%4 = chunk
+    // chunk_slot(row, l%4)), or 1 KB of the packed planes as they lie.
+    // Wave w moves the 1 KB blocks w, w+4, w+8, w+12 of each operand.
+    // Units past the last are issued as zero loads into their free slot.
+    auto issue_unit = [&](int u) {
+      uint8_t* s = smem + (u % kSlots) * kSlot;
+      const bool real = u < u_count;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int blk = wave + 4 * i;
+        const uint32_t row = (uint32_t)(16 * blk + (lane >> 2));
+        const uint32_t kb = (uint32_t)u * kUnitK + 16u * (uint32_t)chunk_slot((int)row, lane & 3);
+        dma16(ra, s + blk * 1024, real && kb < a_lim ? row * (uint32_t)K + kb : kOOB);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int blk = wave + 4 * i;
+        dma16(rw, s + kWOff + blk * 1024,
+              real ? (uint32_t)u * kUnitBytes + (uint32_t)(blk * 1024 + lane * 16) : kOOB);
+      }
+    };
+    // Fragments of a unit: for k-step s, lane (lh, lr) takes the 16 bytes
+    // of K 32 s + 16 lh .. +15 of row 32 i + lr of the wave's activation
+    // rows (tile i) and of plane row 32 j + lr (tile j).  Bit 2 of those
+    // rows is bit 2 of lr, so one swizzle serves all.
+    struct Frag {
+      i32x4 a[2][kFM];
+      i32x4 w[2][kFN];
+    };
+    auto read_unit = [&](int u, Frag& f) {
+      const uint8_t* s = smem + (u % kSlots) * kSlot;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int off = 16 * chunk_slot(lr, 2 * ks + lh);
+#pragma unroll
+        for (int i = 0; i < kFM; ++i)
+          f.a[ks][i] = *reinterpret_cast<const i32x4*>(s + (64 * wave + 32 * i + lr) * 64 + off);
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+          f.w[ks][j] = *reinterpret_cast<const i32x4*>(s + kWOff + (32 * j + lr) * 64 + off);
+      }
+    };
+    auto pin_frag = [](Frag& f) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) asm volatile("" : "+v"(f.a[ks][i]));
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) asm volatile("" : "+v"(f.w[ks][j]));
+      }
+    };
+    auto barrier = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto wait_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    // MFMA issued as W x A^T: accumulator r of tile (i, j) is output row
+    // 32 i + lr of the wave's rows and plane row 32 j + 8 (r/4) + 4 lh + r%4.
+    // The next unit's 20 fragment reads are interleaved with the 32 MFMAs.
+    auto compute = [&](Frag& cur, int u_next, Frag& nxt) {
+      pin_frag(cur);
+      read_unit(u_next, nxt);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < kFM; ++i)
+#pragma unroll
+          for (int j = 0; j < kFN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.w[ks][j], cur.a[ks][i],
+                                                              acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 2 * kFM * kFN; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        if (x < 2 * (kFM + kFN)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      pin_frag(nxt);
+    };
+    // Unit u: wait for this wave's DMA of unit u+1 (units u+2, u+3 may still
+    // be in flight) and for its reads of unit u (done one unit earlier);
+    // after the barrier unit u+1 is visible to every wave and no wave reads
+    // the slot of unit u any more, so it takes unit u + kSlots.
+    auto sync_unit = [&](int u) {
+      wait_vm<(kSlots - 2) * kLoads>();
+      wait_lds();
+      barrier();
+      issue_unit(u + kSlots);
+    };
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) issue_unit(u);
+    wait_vm<(kSlots - 1) * kLoads>();
+    barrier();
+    Frag f0, f1;
+    read_unit(0, f0);
+    if constexpr (kFactors) put_factors();
+    for (int u = 0; u < u_count; u += 2) {
+      sync_unit(u);
+      compute(f0, u + 1, f1);
+      sync_unit(u + 1);
+      compute(f1, u + 2, f0);
+    }
+    wait_vm<0>();       // no DMA into LDS outlives the workgroup
+    wait_lds();
+    __syncthreads();    // every wave is past its last read of the ring
+
+    if constexpr (kMode == kSlice) {
+      // partial sums of this slice: chunk (i, j, r4) of lane l of wave w at
+      // i32x4 index (w * 64 + chunk) * 64 + l of the slice's kPartTile ints
+      i32x4* const mine = reinterpret_cast<i32x4*>(g.part) +
+                          ((size_t)(logical - g.main_tiles) * g.splits + slice) * (kPartTile / 4) +
+                          wave * 4096 + lane;
+#pragma unroll
+      for (int i = 0; i < kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            mine[((i * kFN + j) * 4 + r4) * 64] =
+                i32x4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                      acc[i][j][4 * r4 + 3]};
+      return;
+    }
+  } else {
+    // the tile's sums over its K slices (integer sums: exact in any order)
+    const i32x4* const base = reinterpret_cast<const i32x4*>(g.part) +
+                              (size_t)(logical - g.main_tiles) * g.splits * (kPartTile / 4) +
+                              wave * 4096 + lane;
+    const int ns = g.splits;
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        i32x4 v[4][kMaxSplits];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int sl = 0; sl < kMaxSplits; ++sl)
+            v[r4][sl] = sl < ns ? base[(size_t)sl * (kPartTile / 4) + ((i * kFN + j) * 4 + r4) * 64]
+                                : i32x4{0, 0, 0, 0};
+        i32x16 tot;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          i32x4 sum = v[r4][0];
+#pragma unroll
+          for (int sl = 1; sl < kMaxSplits; ++sl) sum += v[r4][sl];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) tot[4 * r4 + t] = sum[t];
+        }
+        // into the accumulation registers through an MFMA with zero operands
+        const i32x4 z = {0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(z, z, tot, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+
+  if constexpr (kMode != kSlice) {
+    if constexpr (kEpi == kEpiAcc) {
+      // H (hi plane, tiles j >= 4) and L (lo plane) as they are
+#pragma unroll
+      for (int i = 0; i < kFM; ++i) {
+        const int64_t row = wave_row0 + 32 * i + lr;
+#pragma unroll
+        for (int j = 0; j < kFN / 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t col = n0 + 32 * j + 8 * (r >> 2) + 4 * lh + (r & 3);
+            if (row < e.M && col < e.N) {
+              g.acc_lo[row * e.N + col] = acc[i][j][r];
+              g.acc_hi[row * e.N + col] = acc[i][j + kFN / 2][r];
+            }
+          }
+      }
+    } else {
+      // 256 H + L in float32 (one rounding: fmaf of two exact conversions
+      // while |H|, |L| < 2^24), times 2^(X[n] - 1) of the column; the row
+      // scale s_a s_Tw is the epilogue's rs.
+      float rs[kFM];
+#pragma unroll
+      for (int i = 0; i < kFM; ++i) rs[i] = rows[64 * wave + 32 * i + lr];
+      f32x4 cf[kFN / 2][4];
+#pragma unroll
+      for (int j = 0; j < kFN / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          cf[j][q] = *reinterpret_cast<const f32x4*>(colf + 32 * j + 8 * q + 4 * lh);
+      f32x16 accf[kFM][kFN / 2];
+#pragma unroll
+      for (int j = 0; j < kFN / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < kFM; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              accf[i][j][4 * q + t] = __builtin_fmaf((float)acc[i][j + kFN / 2][4 * q + t], 256.0f,
+                                                     (float)acc[i][j][4 * q + t]) *
+                                      cf[j][q][t];
+      store_tile<kEpi, kFM>(accf, rs, wave_row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host --
+
+namespace {
+
+struct SplitPlan {
+  int main_tiles, tail, splits, split_units;
+};
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  const int units = (int)units_of(K);
+  const int total = (int)(((M + kTileM - 1) / kTileM) * ntiles_of(N));
+  SplitPlan p = {total, 0, 1, units};
+  const int tail = total % kCUs;
+  if (tail == 0 || 2 * tail > kCUs) return p;
+  const int s = min(min(kCUs / tail, kMaxSplits), units / 2);
+  if (s < 2 || units * (s - 1) / s < kSplitMinSaved) return p;
+  p.main_tiles = total - tail;
+  p.tail = tail;
+  p.split_units = (units + s - 1) / s;
+  p.splits = (units + p.split_units - 1) / p.split_units;
+  return p;
+}
+
+hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+template <int kEpi, int kMode>
+void launch_mode(int grid, hipEvent_t before, hipEvent_t after, const I8Args& g, const EpiArgs& e,
+                 hipStream_t st) {
+  if (before || after)
+    hipExtLaunchKernelGGL((qgemm_i8_kernel<kEpi, kMode>), dim3(grid), dim3(kThreads), 0, st,
+                          before, after, 0u, g, e);
+  else
+    hipLaunchKernelGGL((qgemm_i8_kernel<kEpi, kMode>), dim3(grid), dim3(kThreads), 0, st, g, e);
+}
+
+template <int kEpi>
+void launch_one(const I8Args& g, const EpiArgs& e, hipStream_t st) {
+  const int tail = g.mt * g.nt - g.main_tiles;
+  if (g.main_tiles)
+    launch_mode<kEpi, kWhole>(g.grid_main, g_ev_before, tail ? nullptr : g_ev_after, g, e, st);
+  if (!tail) return;
+  launch_mode<kEpiPlain, kSlice>(tail * g.splits, g.main_tiles ? nullptr : g_ev_before, nullptr,
+                                 g, e, st);
+  launch_mode<kEpi, kFixup>(tail, nullptr, g_ev_after, g, e, st);
+}
+
+}  // namespace
+
+void set_i8_gemm_events(hipEvent_t before, hipEvent_t after) {
+  g_ev_before = before;
+  g_ev_after = after;
+}
+
+size_t int8_i8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan p = split_plan(M, N, K);
+  return (size_t)p.tail * p.splits * kPartTile * 4;
+}
+
+hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* w8,
+                               const float* w_ts, int64_t M, int64_t N, int64_t K,
+                               const GemmOut& o, void* ws, size_t ws_bytes, int32_t* acc_hi,
+                               int32_t* acc_lo, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  I8Args g = {};
+  g.gate = current_gate();
+  g.a = reinterpret_cast<const uint8_t*>(a_q);
+  g.planes = static_cast<const int8_t*>(w8);
+  const int64_t nt = ntiles_of(N);
+  g.rowf = reinterpret_cast<const float*>(static_cast<const uint8_t*>(w8) +
+                                          r256((size_t)(nt * units_of(K)) * kUnitBytes));
+  g.a_rs = a_s;
+  g.w_ts = w_ts;
+  g.K = K;
+  g.units = (int)units_of(K);
+  g.mt = (int)((M + kTileM - 1) / kTileM);
+  g.nt = (int)nt;
+  const bool split = acc_hi == nullptr && ws_bytes >= int8_i8_gemm_ws_bytes(M, N, K) &&
+                     int8_i8_gemm_ws_bytes(M, N, K) > 0;
+  const SplitPlan p = split ? split_plan(M, N, K) : SplitPlan{g.mt * g.nt, 0, 1, g.units};
+  g.main_tiles = p.main_tiles;
+  g.grid_main = 8 * ((p.main_tiles + 7) / 8);
+  g.splits = p.splits;
+  g.split_units = p.split_units;
+  if (p.tail) g.part = static_cast<int32_t*>(ws);
+  g.acc_hi = acc_hi;
+  g.acc_lo = acc_lo;
+  const int vec = (reinterpret_cast<uintptr_t>(o.y) % 16 == 0) && (o.ldy % 4 == 0);
+  EpiArgs e = {o.y, o.ldy, o.out_f32, o.gelu, o.bias, M, N, vec, o.yq, o.ys, o.y_ts, o.y_amax};
+  if (acc_hi) {
+    launch_one<kEpiAcc>(g, e, st);
+    return hipGetLastError();
+  }
+  int kind = kEpiGeneral;
+  if (o.yq)
+    kind = kEpiQuant;
+  else if (!o.out_f32 && vec)
+    kind = (o.bias ? (o.gelu ? kEpiStagedBiasGelu : kEpiStagedBias)
+                   : (o.gelu ? kEpiStagedGelu : kEpiPlain)) +
+           (o.y_amax ? kEpiAmax : 0);
+  switch (kind) {
+    case kEpiPlain: launch_one<kEpiPlain>(g, e, st); break;
+    case kEpiStagedBias: launch_one<kEpiStagedBias>(g, e, st); break;
+    case kEpiStagedGelu: launch_one<kEpiStagedGelu>(g, e, st); break;
+    case kEpiStagedBiasGelu: launch_one<kEpiStagedBiasGelu>(g, e, st); break;
+    case kEpiAmax + kEpiPlain: launch_one<kEpiAmax + kEpiPlain>(g, e, st); break;
+    case kEpiAmax + kEpiStagedBias: launch_one<kEpiAmax + kEpiStagedBias>(g, e, st); break;
+    case kEpiAmax + kEpiStagedGelu: launch_one<kEpiAmax + kEpiStagedGelu>(g, e, st); break;
+    case kEpiAmax + kEpiStagedBiasGelu: launch_one<kEpiAmax + kEpiStagedBiasGelu>(g, e, st); break;
+    case kEpiQuant: launch_one<kEpiQuant>(g, e, st); break;
+    default: launch_one<kEpiGeneral>(g, e, st); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qact

@@ -4,8 +4,9 @@ Test infrastructure (see the package docstring).
 
 6Bit-Diffusion, abstract: each linear layer's activations are quantized at
 inference time to NVFP4 (temporally stable layers) or INT8 (volatile
-layers); the Fig. 2 caption says DMPQ decides "the quantization bits of
-each linear layer activation".  Table 2 runs the weights at 4 bits ("W4").
+layers); Fig. 2 caption: the DMPQ module chooses the bit width separately
+for the activations of every linear layer.  Table 2 runs the weights at 4
+bits ("W4").
 The pages print no quantizer formula.  The readings taken (all steps in
 float32, in this order; recip(y) is 1/y, or 0 when y == 0):
 

@@ -71,15 +71,15 @@ def test_qlinear_validation():
     assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 9, FAKE, big, None) == -1
     assert _status("qlinear_nvfp4", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
     assert _status("qlinear_nvfp4", None, *ok[1:], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, big, None) == -1
-    assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
-    assert _status("qlinear_int8", *ok[:5], 4, 4, 16, None, ctypes.c_void_p(0x900001), 4, 0, 0, FAKE, big, None) == -3
+    assert _status("qlinear_int8", *ok[:5], None, 4, 4, 16, None, ctypes.c_void_p(0x900000), 4, 0, 0, FAKE, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:5], None, 4, 4, 16, None, ctypes.c_void_p(0x900001), 4, 0, 0, FAKE, big, None) == -3
     # INT8 with K a multiple of 64 reads the weight scales in place, only
     # from a 4-byte aligned array; otherwise the workspace is needed (NVFP4
     # always needs it)
     odd = ctypes.c_void_p(FAKE.value + 1)
     assert _status("qlinear_nvfp4", *ok, 4, 4, 64, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
-    assert _status("qlinear_int8", *ok[:3], odd, FAKE, 4, 4, 64, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
-    assert _status("qlinear_int8", *ok[:5], 4, 4, 80, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:3], odd, FAKE, None, 4, 4, 64, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
+    assert _status("qlinear_int8", *ok[:5], None, 4, 4, 80, None, ctypes.c_void_p(0x900000), 4, 0, 0, None, 0, None) == -5
     # per-tile copies of the E4M3 scales: 4 bytes per row and K unit of 64,
     # rows rounded up to tiles of 256
     units = (1920 + 63) // 64
@@ -100,7 +100,11 @@ def test_qlinear_validation():
     # a full last round (8 x 32 = 256 tiles) or one more than half full
     # (13 x 30 = 390 = 256 + 134) is not split
     assert qa.qlinear_workspace(qa.INT8, 2048, 8192, 7680) == r256(32 * k4 * 1024)
-    assert qa.qlinear_workspace(qa.INT8, 3328, 7680, 7680) == r256(30 * k4 * 1024)
+    # (with the weight's digit planes the INT8 linear runs 256 x 128 tiles:
+    # 13 x 60 = 780 = 3 x 256 + 12, split in 4 slices of int32 partial sums;
+    # the workspace covers both INT8 kernels)
+    assert qa.qlinear_workspace(qa.INT8, 3328, 7680, 7680) == \
+        max(r256(30 * k4 * 1024), 12 * 4 * 256 * 256 * 4)
 
 
 def test_tdc_validation():
@@ -205,7 +209,7 @@ def test_quantized_output_validation():
     # codes overlapping the scales
     assert _status("qlinear_nvfp4_q", *ok, 4, 32, 16, None, 0, FAKE, yq, ctypes.c_void_p(0x900008),
                    FAKE, big, None) == -7
-    assert _status("qlinear_int8_q", *ok[:5], 4, 32, 16, None, 0, FAKE, yq, ys, FAKE, 0, None) == -5
+    assert _status("qlinear_int8_q", *ok[:5], None, 4, 32, 16, None, 0, FAKE, yq, ys, FAKE, 0, None) == -5
 
 
 def test_cosine_helpers_match_oracle():
@@ -248,7 +252,63 @@ def test_amax_output_validation():
                    FAKE, 1 << 20, None) == -3
     assert _status("qlinear_nvfp4_amax", *ok, 4, 4, 16, None, ctypes.c_void_p(0x900008), 4, 0,
                    ctypes.c_void_p(0xA00000), FAKE, 1 << 20, None) == -4
-    assert _status("qlinear_int8_amax", *ok[:5], 4, 4, 16, None, y, 6, 0, ctypes.c_void_p(0xA00000),
+    assert _status("qlinear_int8_amax", *ok[:5], None, 4, 4, 16, None, y, 6, 0, ctypes.c_void_p(0xA00000),
                    FAKE, 1 << 20, None) == -4
-    assert _status("qlinear_int8_amax", *ok[:5], 4, 4, 16, None, y, 4, 0, ctypes.c_void_p(0x900004),
+    assert _status("qlinear_int8_amax", *ok[:5], None, 4, 4, 16, None, y, 4, 0, ctypes.c_void_p(0x900004),
                    FAKE, 1 << 20, None) == -7
+
+
+def test_shape_limits():
+    # 32-bit offsets of a tile's operand rows: K < 2^23; rows below 2^26
+    w = ctypes.c_void_p(0x900000)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    big = 1 << 40
+    for M, N, K in ((4, 4, 1 << 23), (1 << 26, 4, 16), (4, 1 << 26, 16)):
+        assert _status("qlinear_nvfp4", *ok, M, N, K, None, w, N, 0, 0, FAKE, big, None) == -2
+        assert _status("qlinear_int8", *ok[:5], None, M, N, K, None, w, N, 0, 0, FAKE, big,
+                       None) == -2
+    assert _status("act_quant", 1, FAKE, 4, 1 << 23, 1 << 23, w, FAKE, None, 0, None, 0,
+                   None) == -2
+    assert _status("act_quant", 1, FAKE, 1 << 26, 16, 16, w, FAKE, None, 0, None, 0, None) == -2
+    # the largest accepted sizes pass the shape checks (and fail later, on
+    # the workspace, without touching memory)
+    assert _status("qlinear_nvfp4", *ok, 4, 4, (1 << 23) - 16, None, w, 4, 0, 0, FAKE, 0,
+                   None) == -5
+
+
+def test_int8_planes_validation_and_size():
+    w8 = ctypes.c_void_p(0x100000)
+    need = qa.int8_weight_planes_bytes(5760, 1920)
+    r256 = lambda b: (b + 255) // 256 * 256
+    # 45 weight-row tiles of 128 x 30 units of 64, 16 KB each (two digit
+    # planes of 128 rows x 64 bytes), then one float per padded row and the
+    # irregular-row counter
+    assert need == r256(45 * 30 * 16384) + r256(45 * 128 * 4) + 256
+    assert qa.int8_weight_planes_bytes(4, 24) == 0
+    cnt = ctypes.c_int64(0)
+    pcnt = ctypes.addressof(cnt)
+    assert _status("int8_weight_planes", None, FAKE, 4, 16, w8, 1 << 20, pcnt, None) == -1
+    assert _status("int8_weight_planes", FAKE, FAKE, 4, 24, w8, 1 << 20, pcnt, None) == -2
+    assert _status("int8_weight_planes", FAKE, FAKE, 4, 16, ctypes.c_void_p(0x100010), 1 << 20,
+                   pcnt, None) == -3
+    assert _status("int8_weight_planes", FAKE, FAKE, 4, 16, w8, 64, pcnt, None) == -5
+    assert _status("int8_weight_planes", FAKE, FAKE, 4, 16, FAKE, 1 << 20, pcnt, None) == -7
+
+
+def test_int8_acc_and_w8_validation():
+    w8 = ctypes.c_void_p(0x100000)
+    y = ctypes.c_void_p(0x900000)
+    assert _status("qlinear_int8_acc", None, w8, 4, 4, 16, y, y, None) == -1
+    assert _status("qlinear_int8_acc", FAKE, w8, 4, 4, 1 << 17, FAKE, FAKE, None) == -2
+    assert _status("qlinear_int8_acc", FAKE, ctypes.c_void_p(0x100010), 4, 4, 16,
+                   ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000), None) == -3
+    assert _status("qlinear_int8_acc", FAKE, w8, 4, 4, 16, ctypes.c_void_p(0x2000000),
+                   ctypes.c_void_p(0x2000010), None) == -7
+    # with w8 the NVFP4 weight pointers may be null and no workspace is needed
+    assert _status("qlinear_int8", FAKE, FAKE, None, None, FAKE, ctypes.c_void_p(0x100010), 4, 4,
+                   16, None, y, 4, 0, 0, None, 0, None) == -3
+    assert _status("qlinear_int8", FAKE, FAKE, None, None, FAKE, None, 4, 4, 16, None, y, 4, 0,
+                   0, None, 0, None) == -1
+    # the layer call takes w8 for INT8 only
+    assert _status("qlinear", 0, FAKE, 16, FAKE, 0, FAKE, FAKE, FAKE, w8, 4, 4, 16, None, y, 4,
+                   0, 0, FAKE, 1 << 30, None) == -1
