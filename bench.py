@@ -7,7 +7,8 @@ up.  The pages measure on VBench with trained CogVideoX weights; seeded
 synthetic tensors of the same shapes stand in for them.
 
 One step is one pass of the whole hot path over that batch:
-  act_quant NVFP4 -> qlinear_nvfp4 ; act_quant INT8 -> qlinear_int8 ;
+  act_quant NVFP4 -> qlinear_nvfp4 ; act_quant INT8 -> qlinear_int8 (integer
+  MFMA on the weight's int8 digit planes, made once at set-up) ;
   tdc_update (Delta cache, with Gamma and relative-L2 sums) ;
   tdc_apply (the skip path, with Gamma sums) ;
   copy of the sums to the host, dmpq_mask and tdc_decide.
@@ -82,6 +83,36 @@ def measured_traffic(kernel):
     return rec["hbm_bytes_per_launch"]
 
 
+def measured_mfma(kernel):
+    """MFMA counters of `kernel` from profiles/mfma_counters.json (one
+    rocprofv3 --pmc pass: SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs and
+    GRBM_GUI_ACTIVE over the 8 XCDs, per dispatch), or None when the file is
+    missing or the kernel source changed since: the fraction of the kernel's
+    SIMD cycles in which the MFMA unit was busy, and the shader clock
+    implied by the GPU-active cycles and the dispatch's duration."""
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "mixed_precision_quantized_act_amd", "csrc", rec["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return {"mfma_busy_frac": rec["mfma_busy_frac"], "sclk_MHz": rec["sclk_MHz"],
+            "issued_ops_per_s": rec.get("issued_TOP_per_s")}
+
+
+# The pages' own figures (6Bit-Diffusion, abstract and Table 2): end-to-end
+# speed-ups of W4A6 DMPQ and DMPQ + TDC over W16A16, and the memory
+# reduction, on a machine the pages do not name.  Context only.
+PAGES_CONTEXT = {"dmpq_speedup_vs_w16a16": 1.36, "full_speedup_vs_w16a16": 1.92,
+                 "memory_reduction_vs_fp16": 3.32, "hardware": "not stated on the pages",
+                 "source": "6Bit-Diffusion abstract; Table 2"}
+
+
 def cpu_baseline(x, w, x_out, delta_prev, rows):
     """The oracle, untuned, on the first `rows` token rows of the workload."""
     import numpy as np
@@ -133,6 +164,8 @@ def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
                      qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K), dev), stream=stream)
         a8, s8 = qa.empty_int8_act(M, K, dev)
         qa.act_quant(qa.INT8, x, a8, s8, stream=stream)
+        w8 = qa.empty_int8_planes(N, K, dev)
+        qa.int8_weight_planes(wq, ws_, w8, N, K, stream=stream)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         g4 = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, N, K), dev)
@@ -141,7 +174,9 @@ def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
             "nvfp4": lambda: qa.qlinear_nvfp4(aq, asc, ats, wq, ws_, wts, y, M, N, K, epi=epi,
                                               ws=g4, stream=stream),
             "int8": lambda: qa.qlinear_int8(a8, s8, wq, ws_, wts, y, M, N, K, epi=epi, ws=g8,
-                                            stream=stream)}
+                                            stream=stream, w8=w8),
+            "int8_fp16_kernel": lambda: qa.qlinear_int8(a8, s8, wq, ws_, wts, y, M, N, K, epi=epi,
+                                                        ws=g8, stream=stream)}
         rec = {"N": N, "K": K}
         for fmt, fn in calls.items():
             fn()
@@ -155,10 +190,12 @@ def layer_rates(qa, torch, np, dev, stream, M, H, F_, reps=5):
                 ts.append(e0.elapsed_time(e1) * 1e3)
             us = float(np.median(ts))
             tfs = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            own = PEAK["fp4_TFLOPs"] if fmt == "nvfp4" else PEAK["int8_TOPs"]
             rec[fmt] = {"us": round(us, 1), "TFLOP/s": round(tfs, 1),
+                        "frac_own_dtype_peak": round(tfs / own, 4),
                         "frac_fp16_peak": round(tfs / PEAK["bf16_TFLOPs"], 4)}
         out[name] = rec
-        del w, x, y, aq, asc, a8, g4, g8
+        del w, x, y, aq, asc, a8, g4, g8, w8
     return out
 
 
@@ -182,7 +219,9 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
         q, sc, ts = qa.empty_nvfp4(N, KK, dev)
         qa.act_quant(qa.NVFP4, to(w), q, sc, ts, 0,
                      qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, KK), dev), stream=stream)
-        ws.append((q, sc, ts, N, KK))
+        w8 = qa.empty_int8_planes(N, KK, dev)
+        qa.int8_weight_planes(q, sc, w8, N, KK, stream=stream)
+        ws.append((q, sc, ts, N, KK, w8))
     h = torch.empty((M, F_), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     a4 = qa.empty_nvfp4(M, F_, dev)
@@ -192,7 +231,7 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
                            for w in ws), dev)
 
     def lin(fmt, xin, w, out, gelu):
-        q, sc, ts, N, KK = w
+        q, sc, ts, N, KK, w8 = w
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         if fmt == 0:
             aq = a4[0].view(-1)[: M * KK // 2].view(M, KK // 2)
@@ -203,7 +242,8 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
         else:
             aq = a8[0].view(-1)[: M * KK].view(M, KK)
             qa.act_quant(qa.INT8, xin, aq, a8[1], stream=stream)
-            qa.qlinear_int8(aq, a8[1], q, sc, ts, out, M, N, KK, epi=epi, ws=gws, stream=stream)
+            qa.qlinear_int8(aq, a8[1], q, sc, ts, out, M, N, KK, epi=epi, ws=gws, stream=stream,
+                            w8=w8)
 
     def ffn(fu, fd):
         lin(fu, xd, ws[0], h, True)
@@ -215,7 +255,7 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
         # NVFP4 down projection whose tensor amax comes from the up GEMM's
         # epilogue (qlinear_*_amax into act_quant's workspace, QA_AMAX_GIVEN)
         amax_word.zero_()
-        q, sc, ts, N, KK = ws[0]
+        q, sc, ts, N, KK, w8 = ws[0]
         if fu == 0:
             aq = a4[0].view(-1)[: M * K // 2].view(M, K // 2)
             asc = a4[1].view(-1)[: M * K // 16].view(M, K // 16)
@@ -228,8 +268,8 @@ def ffn_section(qa, torch, np, dev, stream, reps=5):
             aq = a8[0].view(-1)[: M * K].view(M, K)
             qa.act_quant(qa.INT8, xd, aq, a8[1], stream=stream)
             qa.qlinear_int8_amax(aq, a8[1], q, sc, ts, h, amax_word, M, N, KK,
-                                 epi=qa.EPI_GELU_TANH, ws=gws, stream=stream)
-        q, sc, ts, N, KK = ws[1]
+                                 epi=qa.EPI_GELU_TANH, ws=gws, stream=stream, w8=w8)
+        q, sc, ts, N, KK, _ = ws[1]
         aq = a4[0].view(-1)[: M * KK // 2].view(M, KK // 2)
         asc = a4[1].view(-1)[: M * KK // 16].view(M, KK // 16)
         qa.act_quant(qa.NVFP4, h.view(torch.int16), aq, asc, a4[2], qa.AMAX_GIVEN, qws,
@@ -318,7 +358,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             w = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
             q, sc, ts = qa.empty_nvfp4(N, K, dev)
             qa.act_quant(qa.NVFP4, w.view(torch.int16), q, sc, ts, 0, qw)
-            lay.append((q, sc, ts, N, K))
+            w8 = qa.empty_int8_planes(N, K, dev)
+            qa.int8_weight_planes(q, sc, w8, N, K)
+            lay.append((q, sc, ts, N, K, w8))
         layers.append(lay)
     bf = torch.bfloat16
     qkv = torch.empty((M, 3 * H), dtype=bf, device=dev)
@@ -353,7 +395,7 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     lay_up = [None, None]
 
     def linear(fmt, x, ldx, lay, y, gelu, stream=stream, amax_out=None, amax_ws=None):
-        q, sc, ts, N, K = lay
+        q, sc, ts, N, K, w8 = lay
         xv = torch.as_strided(x, (M, K), (ldx, 1))
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         if fmt == 0:
@@ -376,9 +418,10 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             qa.act_quant(qa.INT8, i16(xv), aq, a8[1], M=M, K=K, ldx=ldx, stream=stream)
             if amax_out is not None:
                 qa.qlinear_int8_amax(aq, a8[1], q, sc, ts, y, amax_out, M, N, K, epi=epi, ws=gws,
-                                     stream=stream)
+                                     stream=stream, w8=w8)
             else:
-                qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream)
+                qa.qlinear_int8(aq, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws, stream=stream,
+                                w8=w8)
 
     def ffn_pair(l, fu, fd, stream=stream):
         """up (GELU) and down projections of block l; the up GEMM also
@@ -662,6 +705,8 @@ def main():
 
     wq, wsc, wts = qa.empty_nvfp4(N, K, dev)
     qa.act_quant(qa.NVFP4, wd, wq, wsc, wts, 0, qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K), dev))
+    w8 = qa.empty_int8_planes(N, K, dev)           # the INT8 path's digit planes (set-up)
+    qa.int8_weight_planes(wq, wsc, w8, N, K)
     aq, asc, ats = qa.empty_nvfp4(M, K, dev)
     qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K), dev)
     a8, s8 = qa.empty_int8_act(M, K, dev)
@@ -713,7 +758,7 @@ def main():
             aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4, stream=stream)))
         call("act_quant_int8", lambda: qa.act_quant(qa.INT8, xd, a8, s8, stream=stream))
         call("qlinear_int8", lambda: gemm("gemm_int8", lambda: qa.qlinear_int8(
-            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)))
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream, w8=w8)))
         call("tdc_update", lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream))
         call("tdc_apply", lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream))
         host_sums.copy_(sums, non_blocking=True)
@@ -802,6 +847,31 @@ def main():
                       "algorithmic_bytes": int(nbytes)}
     del scratch
 
+    # the INT8 linear on its two kernels, each GEMM dispatch timed by its own
+    # start/end timestamps (median of 9): integer MFMA on the weight's digit
+    # planes (the path above) and fp16 MFMA on operands expanded on load
+    def gemm_us(fn, reps=9):
+        out = []
+        for _ in range(reps):
+            a, b = hip.event(), hip.event()
+            qa.set_gemm_events(a.value, b.value)
+            fn()
+            qa.set_gemm_events(None, None)
+            torch.cuda.synchronize()
+            out.append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        return float(np.median(out)) * 1e3
+    int8_ab = {
+        "i8_mfma_digit_planes_us": round(gemm_us(lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream, w8=w8)), 1),
+        "fp16_mfma_expanded_us": round(gemm_us(lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)), 1),
+        "nvfp4_fp16_mfma_us": round(gemm_us(lambda: qa.qlinear_nvfp4(
+            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4, stream=stream)), 1)}
+    for k_ in list(int8_ab):
+        int8_ab[k_.replace("_us", "_TOP/s")] = round(2.0 * M * N * K / (int8_ab[k_] * 1e-6) / 1e12, 1)
+
     # producer-fused activation quantization: the FFN up-projection
     # (17776 x 1920 -> 7680, GELU) writing its output as NVFP4 (given tensor
     # scale) for the down-projection, against the bf16 output followed by
@@ -887,13 +957,14 @@ def main():
     kern = {
         "gemm_nvfp4": {"us": avg["gemm_nvfp4"] * 1e3, "TFLOP/s": tf(avg["gemm_nvfp4"]),
                        "issued_dtype": "fp16 MFMA on NVFP4 dequantized exactly on load",
-                       "frac_fp16_peak": tf(avg["gemm_nvfp4"]) / PEAK["bf16_TFLOPs"],
-                       "frac_fp4_peak": tf(avg["gemm_nvfp4"]) / PEAK["fp4_TFLOPs"]},
+                       "frac_fp4_peak": tf(avg["gemm_nvfp4"]) / PEAK["fp4_TFLOPs"],
+                       "frac_fp16_peak": tf(avg["gemm_nvfp4"]) / PEAK["bf16_TFLOPs"]},
         "qlinear_nvfp4_call": {"us": avg["qlinear_nvfp4"] * 1e3, "TFLOP/s": tf(avg["qlinear_nvfp4"])},
-        "gemm_int8": {"us": avg["gemm_int8"] * 1e3, "TFLOP/s": tf(avg["gemm_int8"]),
-                      "issued_dtype": "fp16 MFMA on int8 and NVFP4 dequantized exactly on load",
-                      "frac_fp16_peak": tf(avg["gemm_int8"]) / PEAK["bf16_TFLOPs"],
-                      "frac_int8_peak": tf(avg["gemm_int8"]) / PEAK["int8_TOPs"]},
+        "gemm_int8": {"us": avg["gemm_int8"] * 1e3, "TOP/s": tf(avg["gemm_int8"]),
+                      "issued_dtype": "i8 MFMA, int32 sums, against the weight's two int8 "
+                                      "digit planes (2 issued ops per algorithmic op)",
+                      "frac_int8_peak": tf(avg["gemm_int8"]) / PEAK["int8_TOPs"],
+                      "frac_int8_peak_issued": 2 * tf(avg["gemm_int8"]) / PEAK["int8_TOPs"]},
         "qlinear_int8_call": {"us": avg["qlinear_int8"] * 1e3, "TOP/s": tf(avg["qlinear_int8"])},
         "act_quant_nvfp4": {"us": avg["act_quant_nvfp4"] * 1e3,
                             "GB/s": gbs(2.5625 * n, avg["act_quant_nvfp4"])},
@@ -909,24 +980,52 @@ def main():
             if isinstance(v[kk], float):
                 v[kk] = round(v[kk], 4)
 
-    # dominant kernel: the longest of the two GEMM kernels
-    # (both issue fp16 MFMAs: peak = the dense fp16/bf16 figure)
+    # dominant kernel: the longer of the two GEMM kernels, against the peak
+    # of its own contraction's dtype (INT8: 5.0 POP/s; NVFP4 x NVFP4: the FP4
+    # figure, 10.1 PFLOP/s); `issued` gives the fraction of the peak of the
+    # MFMA actually issued (INT8: i8 at twice the algorithmic ops; NVFP4:
+    # fp16, 2.5 PFLOP/s)
     dom = "gemm_int8" if avg["gemm_int8"] >= avg["gemm_nvfp4"] else "gemm_nvfp4"
-    ach, peak, dt = tf(avg[dom]), PEAK["bf16_TFLOPs"], "fp16"
+    ach = tf(avg[dom])
+    if dom == "gemm_int8":
+        peak, unit, dt = PEAK["int8_TOPs"], "TOP/s", "int8"
+        issued = {"dtype": "i8 (two digit planes)", "peak": PEAK["int8_TOPs"],
+                  "frac": round(2 * ach / PEAK["int8_TOPs"], 4)}
+    else:
+        peak, unit, dt = PEAK["fp4_TFLOPs"], "TFLOP/s", "nvfp4"
+        issued = {"dtype": "fp16", "peak": PEAK["bf16_TFLOPs"],
+                  "frac": round(ach / PEAK["bf16_TFLOPs"], 4)}
     roofline = {"bound": "mfma", "kernel": dom, "dtype": dt, "achieved": round(ach, 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(dom)}
+                "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom), "issued": issued,
+                "counters": measured_mfma(dom)}
+    # memory per weight element: bf16 2 B; NVFP4 0.5 B codes + 1/16 B scales;
+    # the INT8 path's digit planes 2 B more (kept beside the NVFP4 weight)
+    context = {"pages": PAGES_CONTEXT,
+               "this_run": {
+                   "weight_bytes_per_param": {"bf16": 2.0, "nvfp4": 0.5625,
+                                              "int8_digit_planes": 2.0},
+                   "weight_memory_ratio_bf16_over_nvfp4": round(2.0 / 0.5625, 3)}}
+    if stack:
+        context["this_run"]["stack_2b_full_vs_dmpq_at_delta_0.05"] = stack["full_vs_dmpq_speedup"]
+        if "full_at_median_d_vs_dmpq_speedup" in stack:
+            context["this_run"]["stack_2b_full_vs_dmpq_at_median_d"] = \
+                stack["full_at_median_d_vs_dmpq_speedup"]
+        context["this_run"]["stack_2b_dmpq_vs_uniform_w4a8"] = round(
+            stack["w4a8"]["ms_per_step"] / stack["dmpq"]["ms_per_step"], 3)
 
     line = {
         "metric": "qlinear TFLOP/s (NVFP4 & INT8 A-paths) + quant/TDC GB/s, % of roofline",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4+int8 (fp16 MFMA)",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4+int8 (NVFP4: fp16 MFMA on exact values; INT8: i8 MFMA, int32)",
         "data": "synthetic",
         "config": {"workload": "cogvideox2b-qkv", "M": M, "K": K, "N": N,
                    "activations": "N(0,1) bf16, 19 outlier channels x30",
                    "weights": "N(0,0.02^2) -> NVFP4", "parallelism": "none (1 GPU)"},
         "kernels": kern,
+        "int8_kernel_ab": int8_ab,
         "cold": cold,
         "ffn_up_fused_nvfp4_output": ffn_fused,
         "stack_cogvideox2b_shape": stack,
@@ -935,6 +1034,7 @@ def main():
         "stack_cogvideox5b_shape": stack5,
         "stack_launch_bound_256_tokens": small,
         "roofline": roofline,
+        "context": context,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, w, x_out, delta_prev, args.cpu_rows)

@@ -37,7 +37,8 @@ def _qa():
 
 
 class Linear:
-    """One NVFP4 weight [N, K] on the GPU (codes, scales, tensor scale)."""
+    """One NVFP4 weight [N, K] on the GPU (codes, scales, tensor scale) and
+    its int8 digit planes for the INT8 path's integer kernel."""
 
     def __init__(self, w_bf16, keep_bf16=False):
         qa, t = _qa(), torch()
@@ -46,6 +47,8 @@ class Linear:
         self.q, self.s, self.ts = qa.empty_nvfp4(N, K)
         ws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K))
         qa.act_quant(qa.NVFP4, w_bf16, self.q, self.s, self.ts, 0, ws)
+        self.w8 = qa.empty_int8_planes(N, K)
+        qa.int8_weight_planes(self.q, self.s, self.w8, N, K)
         self.w_bf16 = w_bf16 if keep_bf16 else None
         self._deq = None
 
@@ -123,7 +126,7 @@ class Stack:
             s8 = self.a8[1]
             qa.act_quant(qa.INT8, xv, a8, s8, M=M, K=K, ldx=ldx)
             qa.qlinear_int8(a8, s8, lay.q, lay.s, lay.ts, y, M, N, K,
-                            epi=qa.EPI_GELU_TANH if gelu else qa.EPI_NONE, ws=self.gws)
+                            epi=qa.EPI_GELU_TANH if gelu else qa.EPI_NONE, ws=self.gws, w8=lay.w8)
         if check:
             self._check_linear(fmt, xv, lay, y, gelu)
 

@@ -428,6 +428,8 @@ def _run_qout(path, a, wq, b, ts, M, N, K, gelu, fused):
                             bias=bias, epi=epi, ws=ws)
         qa.act_quant(qa.NVFP4, y.view(t.int16), yq, ys, ts_d, qa.TSCALE_GIVEN, None)
     t.cuda.synchronize()
+    if not fused:
+        _run_qout.last_bf16 = host(y)
     return host(yq), host(ys)
 
 
@@ -452,6 +454,11 @@ def test_quantized_output(path, M, N, K, bias, gelu):
     assert rel_fro(got, ref) <= 1e-2
     uc, us = _run_qout(path, a, wq, b, ts, M, N, K, gelu, fused=False)
     assert np.array_equal(codes, uc) and np.array_equal(scales, us)
+    # and directly: the oracle's NVFP4 encoding (given scale) of the
+    # library's own bf16 output equals the fused bytes
+    lc, ls, _ = Q.nvfp4_encode(_run_qout.last_bf16, tscale=ts)
+    np.testing.assert_array_equal(codes, lc)
+    np.testing.assert_array_equal(scales, ls)
 
 
 def test_quantized_output_saturating_scale():
