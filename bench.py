@@ -657,6 +657,126 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     return res
 
 
+def sections(args, qa, torch, np, hip, dev, stream, to_dev, xd, xod, dpd, wq, wsc, wts, w8,
+             aq, asc, ats, qws, a8, s8, y4, y8, ws4, ws8, dnew, applied, s4, s2, rws, M, N, K):
+    """The cold bandwidth kernels, the INT8 kernel A/B and the fused FFN
+    output: (cold, int8_ab, ffn_fused) of the report."""
+    import synth
+    n = M * K
+    # the bandwidth kernels timed cold: before each rep a 1 GiB device read
+    # replaces the contents of L2 and the 256 MB Infinity Cache with clean
+    # lines (after a write, the write-back of its dirty lines would land in
+    # the timed kernel); median of the reps
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    gw = qa.workspace(qa.reduce_workspace(n), dev)
+    gsums = torch.zeros(2, dtype=torch.float64, device=dev)
+    cold_calls = [
+        ("act_quant_nvfp4", 2.5625 * n, lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws,
+                                                             stream=stream)),
+        ("act_quant_nvfp4_given_tscale", 2.5625 * n,
+         lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, qa.TSCALE_GIVEN, None, stream=stream)),
+        ("act_quant_int8", 3.0 * n + 4 * M, lambda: qa.act_quant(qa.INT8, xd, a8, s8, stream=stream)),
+        ("block_gamma", 4.0 * n, lambda: qa.block_gamma(xd, xod, gsums, gw, stream=stream)),
+        ("tdc_update", 8.0 * n, lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream)),
+        ("tdc_apply", 6.0 * n, lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream)),
+    ]
+    cold = {}
+    for name, nbytes, fn in cold_calls:
+        reps = []
+        for r in range(args.cold_reps):
+            scratch.sum()
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            reps.append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        t = float(np.median(reps))
+        cold[name] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4),
+                      "algorithmic_bytes": int(nbytes)}
+    del scratch
+
+    # the INT8 linear on its two kernels, each GEMM dispatch timed by its own
+    # start/end timestamps (median of 9): integer MFMA on the weight's digit
+    # planes (the path above) and fp16 MFMA on operands expanded on load
+    def gemm_us(fn, reps=9):
+        out = []
+        for _ in range(reps):
+            a, b = hip.event(), hip.event()
+            qa.set_gemm_events(a.value, b.value)
+            fn()
+            qa.set_gemm_events(None, None)
+            torch.cuda.synchronize()
+            out.append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        return float(np.median(out)) * 1e3
+    int8_ab = {
+        "i8_mfma_digit_planes_us": round(gemm_us(lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream, w8=w8)), 1),
+        "fp16_mfma_expanded_us": round(gemm_us(lambda: qa.qlinear_int8(
+            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)), 1),
+        "nvfp4_fp16_mfma_us": round(gemm_us(lambda: qa.qlinear_nvfp4(
+            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4, stream=stream)), 1)}
+    for k_ in list(int8_ab):
+        int8_ab[k_.replace("_us", "_TOP/s")] = round(2.0 * M * N * K / (int8_ab[k_] * 1e-6) / 1e12, 1)
+
+    # producer-fused activation quantization: the FFN up-projection
+    # (17776 x 1920 -> 7680, GELU) writing its output as NVFP4 (given tensor
+    # scale) for the down-projection, against the bf16 output followed by
+    # act_quant with the same given scale; median of 9 warm calls each
+    F_ = 7680
+    wu = to_dev(synth.weight(3, 0, F_, K))
+    wuq, wus, wuts = qa.empty_nvfp4(F_, K, dev)
+    qa.act_quant(qa.NVFP4, wu, wuq, wus, wuts, 0, qa.workspace(qa.act_quant_workspace(qa.NVFP4, F_, K), dev))
+    del wu
+    h = torch.empty((M, F_), dtype=torch.bfloat16, device=dev)
+    hq, hs, hts = qa.empty_nvfp4(M, F_, dev)
+    hws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
+    uws = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, F_, K), dev)
+    qa.qlinear_nvfp4(aq, asc, ats, wuq, wus, wuts, h, M, F_, K, epi=qa.EPI_GELU_TANH, ws=uws,
+                     stream=stream)
+    qa.act_quant(qa.NVFP4, h.view(torch.int16), hq, hs, hts, 0, hws, stream=stream)   # a tensor scale
+    torch.cuda.synchronize()
+
+    def timed(fn, reps=9):
+        out = []
+        for _ in range(reps):
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            out.append(hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        return float(np.median(out)) * 1e3
+
+    def unfused():
+        qa.qlinear_nvfp4(aq, asc, ats, wuq, wus, wuts, h, M, F_, K, epi=qa.EPI_GELU_TANH, ws=uws,
+                         stream=stream)
+        qa.act_quant(qa.NVFP4, h.view(torch.int16), hq, hs, hts, qa.TSCALE_GIVEN, None,
+                     stream=stream)
+
+    def fused():
+        qa.qlinear_nvfp4_q(aq, asc, ats, wuq, wus, wuts, hts, hq, hs, M, F_, K,
+                           epi=qa.EPI_GELU_TANH, ws=uws, stream=stream)
+
+    for _ in range(2):
+        unfused()
+        fused()
+    t_un, t_fu = timed(unfused), timed(fused)
+    ffn_fused = {"shape": [M, K, F_], "epilogue": "GELU-tanh",
+                 "unfused_us": round(t_un, 1), "fused_us": round(t_fu, 1),
+                 "unfused_TFLOP/s": round(2.0 * M * F_ * K / (t_un * 1e-6) / 1e12, 1),
+                 "fused_TFLOP/s": round(2.0 * M * F_ * K / (t_fu * 1e-6) / 1e12, 1)}
+    del h, hq, hs
+    return cold, int8_ab, ffn_fused
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -672,6 +792,10 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=9,
                     help="reps of each bandwidth kernel timed after a 1 GiB cache-evicting read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step and report it, without the other sections (cold "
+                         "kernels, INT8 kernel A/B, fused FFN output, stacks, per-layer rates): "
+                         "a short run whose every GEMM launch is the workload's, for profilers")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (counter calibration)")
     args = ap.parse_args()
@@ -811,132 +935,27 @@ def main():
                 hip.destroy(b)
     avg = {k: float(np.mean(v)) for k, v in ev.items() if v}
 
-    # the bandwidth kernels timed cold: before each rep a 1 GiB device read
-    # replaces the contents of L2 and the 256 MB Infinity Cache with clean
-    # lines (after a write, the write-back of its dirty lines would land in
-    # the timed kernel); median of the reps
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    gw = qa.workspace(qa.reduce_workspace(n), dev)
-    gsums = torch.zeros(2, dtype=torch.float64, device=dev)
-    cold_calls = [
-        ("act_quant_nvfp4", 2.5625 * n, lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, 0, qws,
-                                                             stream=stream)),
-        ("act_quant_nvfp4_given_tscale", 2.5625 * n,
-         lambda: qa.act_quant(qa.NVFP4, xd, aq, asc, ats, qa.TSCALE_GIVEN, None, stream=stream)),
-        ("act_quant_int8", 3.0 * n + 4 * M, lambda: qa.act_quant(qa.INT8, xd, a8, s8, stream=stream)),
-        ("block_gamma", 4.0 * n, lambda: qa.block_gamma(xd, xod, gsums, gw, stream=stream)),
-        ("tdc_update", 8.0 * n, lambda: qa.tdc_update(xd, xod, dpd, dnew, s4, rws, stream=stream)),
-        ("tdc_apply", 6.0 * n, lambda: qa.tdc_apply(xd, dnew, applied, s2, rws, stream=stream)),
-    ]
-    cold = {}
-    for name, nbytes, fn in cold_calls:
-        reps = []
-        for r in range(args.cold_reps):
-            scratch.sum()
-            a, b = hip.event(), hip.event()
-            hip.record(a, stream)
-            fn()
-            hip.record(b, stream)
-            torch.cuda.synchronize()
-            reps.append(hip.ms(a, b))
-            hip.destroy(a)
-            hip.destroy(b)
-        t = float(np.median(reps))
-        cold[name] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
-                      "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4),
-                      "algorithmic_bytes": int(nbytes)}
-    del scratch
-
-    # the INT8 linear on its two kernels, each GEMM dispatch timed by its own
-    # start/end timestamps (median of 9): integer MFMA on the weight's digit
-    # planes (the path above) and fp16 MFMA on operands expanded on load
-    def gemm_us(fn, reps=9):
-        out = []
-        for _ in range(reps):
-            a, b = hip.event(), hip.event()
-            qa.set_gemm_events(a.value, b.value)
-            fn()
-            qa.set_gemm_events(None, None)
-            torch.cuda.synchronize()
-            out.append(hip.ms(a, b))
-            hip.destroy(a)
-            hip.destroy(b)
-        return float(np.median(out)) * 1e3
-    int8_ab = {
-        "i8_mfma_digit_planes_us": round(gemm_us(lambda: qa.qlinear_int8(
-            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream, w8=w8)), 1),
-        "fp16_mfma_expanded_us": round(gemm_us(lambda: qa.qlinear_int8(
-            a8, s8, wq, wsc, wts, y8, M, N, K, ws=ws8, stream=stream)), 1),
-        "nvfp4_fp16_mfma_us": round(gemm_us(lambda: qa.qlinear_nvfp4(
-            aq, asc, ats, wq, wsc, wts, y4, M, N, K, ws=ws4, stream=stream)), 1)}
-    for k_ in list(int8_ab):
-        int8_ab[k_.replace("_us", "_TOP/s")] = round(2.0 * M * N * K / (int8_ab[k_] * 1e-6) / 1e12, 1)
-
-    # producer-fused activation quantization: the FFN up-projection
-    # (17776 x 1920 -> 7680, GELU) writing its output as NVFP4 (given tensor
-    # scale) for the down-projection, against the bf16 output followed by
-    # act_quant with the same given scale; median of 9 warm calls each
-    F_ = 7680
-    wu = to_dev(synth.weight(3, 0, F_, K))
-    wuq, wus, wuts = qa.empty_nvfp4(F_, K, dev)
-    qa.act_quant(qa.NVFP4, wu, wuq, wus, wuts, 0, qa.workspace(qa.act_quant_workspace(qa.NVFP4, F_, K), dev))
-    del wu
-    h = torch.empty((M, F_), dtype=torch.bfloat16, device=dev)
-    hq, hs, hts = qa.empty_nvfp4(M, F_, dev)
-    hws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
-    uws = qa.workspace(qa.qlinear_workspace(qa.NVFP4, M, F_, K), dev)
-    qa.qlinear_nvfp4(aq, asc, ats, wuq, wus, wuts, h, M, F_, K, epi=qa.EPI_GELU_TANH, ws=uws,
-                     stream=stream)
-    qa.act_quant(qa.NVFP4, h.view(torch.int16), hq, hs, hts, 0, hws, stream=stream)   # a tensor scale
-    torch.cuda.synchronize()
-
-    def timed(fn, reps=9):
-        out = []
-        for _ in range(reps):
-            a, b = hip.event(), hip.event()
-            hip.record(a, stream)
-            fn()
-            hip.record(b, stream)
-            torch.cuda.synchronize()
-            out.append(hip.ms(a, b))
-            hip.destroy(a)
-            hip.destroy(b)
-        return float(np.median(out)) * 1e3
-
-    def unfused():
-        qa.qlinear_nvfp4(aq, asc, ats, wuq, wus, wuts, h, M, F_, K, epi=qa.EPI_GELU_TANH, ws=uws,
-                         stream=stream)
-        qa.act_quant(qa.NVFP4, h.view(torch.int16), hq, hs, hts, qa.TSCALE_GIVEN, None,
-                     stream=stream)
-
-    def fused():
-        qa.qlinear_nvfp4_q(aq, asc, ats, wuq, wus, wuts, hts, hq, hs, M, F_, K,
-                           epi=qa.EPI_GELU_TANH, ws=uws, stream=stream)
-
-    for _ in range(2):
-        unfused()
-        fused()
-    t_un, t_fu = timed(unfused), timed(fused)
-    ffn_fused = {"shape": [M, K, F_], "epilogue": "GELU-tanh",
-                 "unfused_us": round(t_un, 1), "fused_us": round(t_fu, 1),
-                 "unfused_TFLOP/s": round(2.0 * M * F_ * K / (t_un * 1e-6) / 1e12, 1),
-                 "fused_TFLOP/s": round(2.0 * M * F_ * K / (t_fu * 1e-6) / 1e12, 1)}
-    del h, hq, hs
+    cold = int8_ab = ffn_fused = None
+    if not args.step_only:
+        cold, int8_ab, ffn_fused = sections(args, qa, torch, np, hip, dev, stream, to_dev, xd, xod,
+                                            dpd, wq, wsc, wts, w8, aq, asc, ats, qws, a8, s8,
+                                            y4, y8, ws4, ws8, dnew, applied, s4, s2, rws, M, N, K)
     stack = (stack_section(qa, torch, np, dev, stream, steps=args.stack_steps)
-             if args.stack_steps > 0 else None)
-    ffn3 = ffn_section(qa, torch, np, dev, stream) if args.layer_reps > 0 else None
+             if args.stack_steps > 0 and not args.step_only else None)
+    ffn3 = (ffn_section(qa, torch, np, dev, stream)
+            if args.layer_reps > 0 and not args.step_only else None)
     layers2b = (layer_rates(qa, torch, np, dev, stream, M, 1920, 7680, reps=args.layer_reps)
-                if args.layer_reps > 0 else None)
+                if args.layer_reps > 0 and not args.step_only else None)
     # a launch-bound stack (30 blocks of the single-linear config's width:
     # H 256, FFN 1024, 256 tokens), where the per-step host sync and the
     # launches, not the kernels, set the step time
     small = None
-    if args.stack_steps > 0:
+    if args.stack_steps > 0 and not args.step_only:
         small = stack_section(qa, torch, np, dev, stream, L=30, H=256, F_=1024, M=256,
                               steps=args.stack_steps, cfg=1,
                               modes=("dmpq", "full", "median", "device"))
     stack5 = None
-    if args.stack5_steps > 0:
+    if args.stack5_steps > 0 and not args.step_only:
         stack5 = stack_section(qa, torch, np, dev, stream, L=42, H=3072, F_=12288, M=M,
                                steps=args.stack5_steps, cfg=5,
                                modes=("dmpq", "full", "median", "device"))

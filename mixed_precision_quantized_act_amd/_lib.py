@@ -85,6 +85,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libqact.so is not built at {LIB_PATH}; run "
                               "python -m mixed_precision_quantized_act_amd.build")
+        # torch first: its HIP runtime (listed by torch's libraries as
+        # libamdhip64.so) then provides the libamdhip64.so.7 the library
+        # needs.  Loaded the other way round, the process holds two HIP
+        # runtimes, and whichever touches the GPU second finds no device.
+        import torch  # noqa: F401
         h = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(h, name)
