@@ -62,7 +62,9 @@ typedef enum {
   QA_EUNSUPPORTED = -4,  /* a valid but unimplemented combination         */
   QA_EWORKSPACE = -5,    /* ws_bytes below the required size              */
   QA_EHIP = -6,          /* a HIP launch failed                           */
-  QA_EALIAS = -7         /* an output overlaps an input it must not alias */
+  QA_EALIAS = -7,        /* an output overlaps an input it must not alias */
+  QA_ESCRATCH = -8       /* the call needs more than the library's static
+                            scratch (QA_NOALLOC_SCRATCH_BYTES)            */
 } qa_status;
 
 typedef enum { QA_NVFP4 = 0, QA_INT8 = 1 } qa_fmt;
@@ -166,7 +168,7 @@ int qlinear_int8_q(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
  * 0 <= M, N < 2^26 (QA_ESHAPE otherwise: the kernels address a tile's
  * 256 operand rows with 32-bit offsets below 2^31).
  * ------------------------------------------------------------------------ */
-size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);
+size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K);  /* 0 if rejected */
 int qlinear_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_ts,
                   const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
                   int64_t M, int64_t N, int64_t K, const uint16_t* bias,
@@ -177,6 +179,29 @@ int qlinear_int8(const int8_t* a_q, const float* a_s,
                  int64_t M, int64_t N, int64_t K, const uint16_t* bias,
                  void* y, int64_t ldy, qa_out out, qa_epi epi,
                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* qlinear_int8_noalloc: for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same call as qlinear_int8 -- same arguments without
+ * ws/ws_bytes, same kernels, same outputs bit for bit -- with its
+ * workspace in a device array of the library's own, QA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held from the first call on that GPU until the process
+ * ends.  It allocates nothing: the first call on a device looks up the
+ * array's address there (a symbol query; QA_EHIP if it fails), later calls
+ * reuse it.  A shape whose qlinear_workspace(QA_INT8, M, N, K) exceeds the
+ * array returns QA_ESCRATCH with nothing enqueued (the linears of the
+ * CogVideoX-2B and -5B blocks at 17776 tokens need at most 57 MiB).  A
+ * call that qlinear_int8 would reject returns its status first.  `stream` (NULL: the null
+ * stream) must belong to the current device
+ * (QA_EINVAL otherwise).  Every call on one GPU shares that GPU's array:
+ * calls that may overlap in time there (other streams, other host threads)
+ * race on it and must be serialised by the caller.  No word of the array
+ * needs to start at zero, and it keeps whatever the last call left. */
+#define QA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int qlinear_int8_noalloc(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                         const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                         int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
+                         qa_out out, qa_epi epi, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * INT8 path on integer MFMA.  6Bit-Diffusion, abstract: volatile layers

@@ -15,6 +15,7 @@ OUT_BF16, OUT_F32 = 0, 1
 EPI_NONE, EPI_GELU_TANH = 0, 1
 TSCALE_GIVEN = 1
 AMAX_GIVEN = 2
+NOALLOC_SCRATCH_BYTES = 64 << 20     # QA_NOALLOC_SCRATCH_BYTES
 
 
 class QactError(RuntimeError):
@@ -40,6 +41,8 @@ _SIGS = {
                                      ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
     "qlinear_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                                     ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
+    "qlinear_int8_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
+                                            _I64, ctypes.c_int, ctypes.c_int, _P]),
     "int8_weight_planes_bytes": (_SZ, [_I64, _I64]),
     "int8_weight_planes": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _SZ, _P, _P]),
     "qlinear_int8_acc": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P]),
@@ -165,6 +168,16 @@ def qlinear_int8(a_q, a_s, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, 
     _check("qlinear_int8", lib().qlinear_int8(
         _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias),
         _ptr(y), ldy, out, epi, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def qlinear_int8_noalloc(a_q, a_s, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16,
+                         epi=EPI_NONE, ldy=None, stream=None, w8=None):
+    """qlinear_int8 with its workspace in the library's static device array
+    (NOALLOC_SCRATCH_BYTES per GPU); calls that overlap on one GPU race."""
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("qlinear_int8_noalloc", lib().qlinear_int8_noalloc(
+        _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias),
+        _ptr(y), ldy, out, epi, _stream(stream)))
 
 
 def int8_weight_planes_bytes(N, K):

@@ -80,6 +80,7 @@ const char* qa_strerror(int status) {
     case QA_EWORKSPACE: return "workspace too small";
     case QA_EHIP: return "HIP launch failed";
     case QA_EALIAS: return "an output overlaps an input";
+    case QA_ESCRATCH: return "the call needs more than the library's static scratch (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -138,7 +139,7 @@ static size_t int8_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t qlinear_workspace(qa_fmt fmt, int64_t M, int64_t N, int64_t K) {
-  if (M < 0 || N < 0 || K <= 0) return 0;
+  if (check_mk(M, K) || check_nk(M, N, K)) return 0;
   return fmt == QA_NVFP4 ? nvfp4_gemm_ws_bytes(M, N, K) : int8_ws_bytes(M, N, K);
 }
 
@@ -198,14 +199,27 @@ static hipError_t launch_int8(const int8_t* a_q, const float* a_s, const uint8_t
   return launch_int8_gemm(a_q, a_s, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes, stream);
 }
 
-int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
-                 const float* w_ts, const void* w8, int64_t M, int64_t N, int64_t K,
-                 const uint16_t* bias, void* y, int64_t ldy, qa_out out, qa_epi epi, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+extern "C++" {
+namespace qact {
+// the checks of qlinear_int8 that do not involve the workspace
+int int8_linear_status(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                       const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                       int64_t N, int64_t K, const void* y, int64_t ldy, qa_out out, qa_epi epi) {
   if (!a_q || !a_s || !w_ts) return QA_EINVAL;
   if (int s = check_int8_weight(w_q, w_s, w8)) return s;
   if (int s = check_linear(M, N, K, y, ldy, out, epi)) return s;
   if (!aligned16(a_q)) return QA_EALIGN;
+  return QA_OK;
+}
+}  // namespace qact
+}  // extern "C++"
+
+int qlinear_int8(const int8_t* a_q, const float* a_s, const uint8_t* w_q, const uint8_t* w_s,
+                 const float* w_ts, const void* w8, int64_t M, int64_t N, int64_t K,
+                 const uint16_t* bias, void* y, int64_t ldy, qa_out out, qa_epi epi, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  if (int s = int8_linear_status(a_q, a_s, w_q, w_s, w_ts, w8, M, N, K, y, ldy, out, epi))
+    return s;
   {
     const size_t need = int8_ws_need(M, N, K, w_s, w8);
     if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qact.h"
+
 namespace qact {
 
 // Device-side gate of a call: every kernel of the call reads the byte
@@ -96,6 +98,11 @@ hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* 
 void set_i8_gemm_events(hipEvent_t before, hipEvent_t after);
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
+// qlinear_int8's argument checks other than those of its workspace
+int int8_linear_status(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
+                       const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M,
+                       int64_t N, int64_t K, const void* y, int64_t ldy, qa_out out, qa_epi epi);
+
 size_t reduce_ws_bytes(int64_t n);
 // mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine,
 // 5: tdc_apply that also max-combines |out| into *amax_out

@@ -117,8 +117,27 @@ def test_tdc_validation():
     assert _status("block_gamma", FAKE, FAKE, 64, None, FAKE, 1 << 20, None) == -1
 
 
+def test_noalloc_scratch_limit():
+    """qlinear_int8_noalloc refuses a shape whose workspace exceeds the static
+    scratch before it touches a device, and returns qlinear_int8's status for
+    a rejected shape (its workspace size is then 0)."""
+    assert qa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = (256, 131072, 16384)          # 128 MiB of weight-scale copies
+    assert qa.qlinear_workspace(qa.INT8, *big) > qa.NOALLOC_SCRATCH_BYTES
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert _status("qlinear_int8_noalloc", *args, *big, None, FAKE, big[1], 0, 0, None) == -8
+    assert _status("qlinear_int8_noalloc", *args, 4, 64, 24, None, FAKE, 64, 0, 0, None) == -2
+    assert qa.qlinear_workspace(qa.INT8, 4, 64, 24) == 0
+    assert qa.qlinear_workspace(qa.INT8, 4, 64, 1 << 23) == 0
+    assert _status("qlinear_int8_noalloc", *args, 4, 64, 1 << 23, None, FAKE, 64, 0, 0, None) == -2
+    # the CogVideoX-2B and -5B block linears at 17776 tokens fit
+    for n, k in ((5760, 1920), (7680, 1920), (1920, 7680), (9216, 3072), (3072, 12288),
+                 (12288, 3072)):
+        assert 0 < qa.qlinear_workspace(qa.INT8, 17776, n, k) <= qa.NOALLOC_SCRATCH_BYTES
+
+
 def test_strerror_covers_codes():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert qa.strerror(s) != "unknown status"
 
 
