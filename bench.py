@@ -64,6 +64,16 @@ class Hip:
         self.h.hipEventDestroy(e)
 
 
+def sources_unchanged(rec):
+    """True when the kernel sources a profile record names (sha256 over the
+    files in order) are those in the tree."""
+    h = hashlib.sha256()
+    for name in rec.get("sources", [rec["source"]]):
+        with open(os.path.join(ROOT, "mixed_precision_quantized_act_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest() == rec["source_sha256"]
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from profiles/traffic.json (two
     rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by the same
@@ -74,12 +84,8 @@ def measured_traffic(kernel):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec:
+    if not rec or not sources_unchanged(rec):
         return None
-    src = os.path.join(ROOT, "mixed_precision_quantized_act_amd", "csrc", rec["source"])
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-            return None
     return rec["hbm_bytes_per_launch"]
 
 
@@ -95,14 +101,11 @@ def measured_mfma(kernel):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec:
+    if not rec or not sources_unchanged(rec):
         return None
-    src = os.path.join(ROOT, "mixed_precision_quantized_act_amd", "csrc", rec["source"])
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-            return None
     return {"mfma_busy_frac": rec["mfma_busy_frac"], "sclk_MHz": rec["sclk_MHz"],
-            "issued_ops_per_s": rec.get("issued_TOP_per_s")}
+            "issued_TOP_per_s": rec["issued_TOP_per_s"], "duration_us": rec["duration_us"],
+            "source": "profiles/mfma_counters.json"}
 
 
 # The pages' own figures (6Bit-Diffusion, abstract and Table 2): end-to-end
