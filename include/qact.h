@@ -411,6 +411,21 @@ int qa_decide_step(const double* sums, const float* alpha, const float* beta, do
                    hipStream_t stream);
 int qa_set_gate(const uint8_t* flags, uint32_t bits);
 
+/* Test-only: the element conversions the quantizers and epilogues are built
+ * on, applied to the float32 bit patterns first .. first + count - 1
+ * (count >= 0, first + count <= 2^32), one output per pattern, so that a
+ * test can check them on every input against the format rules (NVFP4:
+ * 6Bit-Diffusion, abstract):
+ *   op 0  E2M1 code (u8 out; low nibble, bit 3 the sign) as the NVFP4
+ *         encoders convert x * inv: nearest, ties to the even code,
+ *         saturating at 6;
+ *   op 1  E4M3FN code (u8 out) of a group scale: inputs must be
+ *         non-negative and finite (patterns <= 0x7F7FFFFF);
+ *   op 2  bf16 bits (u16 out, 2-byte aligned) as the epilogues round
+ *         float32 outputs: nearest, ties to even.
+ * Outputs for NaN or infinite inputs (ops 0 and 2) are not specified. */
+int qa_test_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream);
+
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
  * inside qlinear) launches its main GEMM kernel with hipExtLaunchKernel so
  * that `before` and `after` take that dispatch's start and end timestamps

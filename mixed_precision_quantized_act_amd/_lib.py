@@ -70,6 +70,7 @@ _SIGS = {
     "dmpq_mask": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_double, _P]),
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
     "qa_set_gemm_events": (ctypes.c_int, [_P, _P]),
+    "qa_test_convert": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint32, _I64, _P, _P]),
     "qa_set_gate": (ctypes.c_int, [_P, ctypes.c_uint32]),
     "qa_decide_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_double, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -384,6 +385,14 @@ def cosine_from_sums(sums3):
     if s.size < 3:
         raise ValueError("cosine_from_sums: needs the three sums")
     return lib().qa_cosine_from_sums(s.ctypes.data)
+
+
+def convert_check(op, first, out, count=None, stream=None):
+    """Test-only: the library's element conversion `op` (0 E2M1, 1 E4M3
+    scale, 2 bf16) of the float32 patterns first .. first + count - 1 into
+    the device tensor out (u8, or int16 for bf16)."""
+    count = out.numel() if count is None else count
+    _check("qa_test_convert", lib().qa_test_convert(op, first, count, _ptr(out), _stream(stream)))
 
 
 def set_gemm_events(before, after):

@@ -520,6 +520,16 @@ int delta_cosine(const uint16_t* d_new, const uint16_t* d_prev, int64_t n, doubl
   return hip_status(launch_tdc(4, d_new, d_prev, nullptr, nullptr, n, sums3, ws, stream));
 }
 
+int qa_test_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream) {
+  if (op < 0 || op > 2 || count < 0 || !out) return QA_EINVAL;
+  if ((uint64_t)first + (uint64_t)count > ((uint64_t)1 << 32)) return QA_EINVAL;
+  if (op == 2 && (reinterpret_cast<uintptr_t>(out) & 1u)) return QA_EALIGN;
+  // the E4M3 scale encoder is defined on non-negative finite floats
+  if (op == 1 && count && (uint64_t)first + (uint64_t)count - 1 > 0x7F7FFFFFu) return QA_EINVAL;
+  if (count == 0) return QA_OK;
+  return hip_status(launch_convert(op, first, count, out, stream));
+}
+
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
   set_gemm_events(before, after);

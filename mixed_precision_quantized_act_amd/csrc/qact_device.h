@@ -25,8 +25,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // Two float32 -> packed bfloat16 (a in the low half), round to nearest
-// even, one v_cvt_pk_bf16_f32: equal to f32_to_bf16 on every non-NaN
-// float32 (checked on all 2^32 bit patterns on the GPU).
+// even, one v_cvt_pk_bf16_f32: equal to round-to-nearest-even on every
+// finite float32 (tests/test_gpu_convert.py runs it on all of them through
+// qa_test_convert).
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
@@ -60,7 +61,8 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // first value in the low nibble): nearest of 0,.5,1,1.5,2,3,4,6 with ties
 // to the even code, saturating at 6, bit 3 = the sign bit of the input.
 // gfx950's v_cvt_scalef32_pk_fp4_f32 with a unit scale rounds exactly so
-// (checked against the threshold rule on every finite float32).
+// on every finite float32 (tests/test_gpu_convert.py, through
+// qa_test_convert; e4m3_encode likewise on every non-negative one).
 #define QACT_E2M1_PK(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
 
 // E2M1 codes of the 8 bf16 values of a 16-byte vector times `inv`, as 8

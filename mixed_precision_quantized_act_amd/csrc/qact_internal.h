@@ -48,6 +48,9 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
 hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                              float* scale, hipStream_t stream);
 
+// ---- test-only element conversions (convert_check.hip)
+hipError_t launch_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream);
+
 // ---- profiling hook: events recorded around each main GEMM kernel
 void set_gemm_events(hipEvent_t before, hipEvent_t after);
 

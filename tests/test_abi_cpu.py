@@ -136,6 +136,18 @@ def test_noalloc_scratch_limit():
         assert 0 < qa.qlinear_workspace(qa.INT8, 17776, n, k) <= qa.NOALLOC_SCRATCH_BYTES
 
 
+def test_convert_check_validation():
+    # the test-only conversion entry point rejects bad arguments before any launch
+    assert _status("qa_test_convert", 3, 0, 16, FAKE, None) == -1
+    assert _status("qa_test_convert", 0, 0, -1, FAKE, None) == -1
+    assert _status("qa_test_convert", 0, 0xFFFFFFF0, 17, FAKE, None) == -1
+    assert _status("qa_test_convert", 0, 0, 16, None, None) == -1
+    assert _status("qa_test_convert", 2, 0, 16, ctypes.c_void_p(0x10001), None) == -3
+    assert _status("qa_test_convert", 1, 0x7F7FFFF0, 17, FAKE, None) == -1   # past the finite range
+    assert _status("qa_test_convert", 1, 0x80000000, 1, FAKE, None) == -1    # negative scale
+    assert _status("qa_test_convert", 0, 5, 0, FAKE, None) == 0              # nothing to do
+
+
 def test_strerror_covers_codes():
     for s in range(-8, 1):
         assert qa.strerror(s) != "unknown status"

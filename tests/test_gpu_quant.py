@@ -158,3 +158,44 @@ def test_deterministic_repeat():
     b = gpu_nvfp4(x)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+
+def _nvfp4_with(x, M, K, ldx=None):
+    """act_quant NVFP4 of the first K columns of x (rows of ldx elements);
+    returns codes, scales, tensor scale (host)."""
+    qa, t = _qa(), torch()
+    codes, scales, ts = qa.empty_nvfp4(M, K)
+    ws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K))
+    qa.act_quant(qa.NVFP4, dev(x), codes, scales, ts, 0, ws, M=M, K=K,
+                 ldx=K if ldx is None else ldx)
+    t.cuda.synchronize()
+    return host(codes), host(scales), np.float32(host(ts)[0])
+
+
+def test_nvfp4_strided_equals_contiguous_full_shape():
+    # the QKV activation contiguous (one flat tensor-max sweep) and at a
+    # padded row stride (row-by-row sweep) whose padding holds a huge value:
+    # the same bytes, the padding never entering the tensor maximum
+    x, _ = synth.linear_case(2)
+    M, K = x.shape
+    one = _nvfp4_with(x, M, K)
+    pad = np.zeros((M, K + 16), np.uint16)
+    pad[:, :K] = x
+    pad[:, K:] = 0x7F7F
+    two = _nvfp4_with(pad, M, K, ldx=K + 16)
+    for a, b in zip(one, two):
+        np.testing.assert_array_equal(a, b)
+    assert one[2] == Q.nvfp4_tensor_scale(x)
+
+
+def test_nvfp4_5b_hidden_shape_sampled_rows():
+    # a CogVideoX-5B block input (17776 x 3072, 19 outlier channels x30)
+    M, K = 17776, 3072
+    x = synth.activations(5, M, K, "normal", 19, 30.0)
+    c, s, ts = _nvfp4_with(x, M, K)
+    assert ts == Q.nvfp4_tensor_scale(x)
+    rows = sample_rows(M, 256, seed=3)
+    oc, os_, _ = Q.nvfp4_encode(x[rows], tscale=ts)
+    np.testing.assert_array_equal(s[rows], os_)
+    np.testing.assert_array_equal(c[rows], oc)
