@@ -198,8 +198,7 @@ struct RawWords<true> {
 // workgroup, storing its fp32 partial sums; kFixup -- one workgroup per tail
 // tile, adding the slices' partial sums (in slice order) and running the
 // epilogue.  Each is its own kernel so that the whole-tile kernel carries
-// none of the slice bookkeeping.
-enum { kWhole = 0, kSlice = 1, kFixup = 2 };
+// none of the slice bookkeeping (modes kWhole, kSlice, kFixup).
 
 template <bool I8, int kEpi, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -214,26 +213,12 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
   // tile-rows at a time so that concurrent tiles share A rows and B rows.
   // A kSlice workgroup computes slice `slice` of tail tile main_tiles +
   // bid / splits: raw units u_begin .. u_begin + u_count - 1.
-  const int bid = (int)blockIdx.x;
-  int logical, slice = 0, u_begin = 0, u_count = g.units;
-  if constexpr (kMode == kWhole) {
-    const int per_xcd = (g.main_tiles + 7) / 8;
-    logical = (bid & 7) * per_xcd + (bid >> 3);
-    if (logical >= g.main_tiles) return;
-  } else if constexpr (kMode == kSlice) {
-    logical = g.main_tiles + bid / g.splits;
-    slice = bid % g.splits;
-    u_begin = slice * g.split_units;
-    u_count = min(g.units - u_begin, g.split_units);
-  } else {
-    logical = g.main_tiles + bid;
-  }
-  const int group = logical / (kGroupM * g.nt);
-  const int first_m = group * kGroupM;
-  const int gsz = min(g.mt - first_m, kGroupM);
-  const int in_group = logical - group * kGroupM * g.nt;
-  const int tm = first_m + in_group % gsz;
-  const int tn = in_group / gsz;
+  TileWork tw;
+  if (!tile_work(kMode, (int)blockIdx.x, g.main_tiles, g.splits, g.split_units, g.units, tw))
+    return;
+  const int logical = tw.logical, slice = tw.slice, u_begin = tw.u_begin, u_count = tw.u_count;
+  int tm, tn;
+  tile_coords(logical, g.mt, g.nt, kGroupM, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -599,27 +584,14 @@ static size_t r256(size_t v) { return (v + 255) / 256 * 256; }
 // is only less well fitted.  Every slice stores its fp32 partial sums in the workspace;
 // a second launch adds them per tail tile and runs the epilogue (no
 // workgroup waits for another inside a launch).
-struct SplitPlan {
-  int main_tiles, tail, splits, split_units;
-};
+// (the split is worth it only if the round gets shorter by more than the
+// slice and fixup launches cost: measured, the fixup alone takes about as
+// long as 15-20 raw units of a tile -- the QKV shape, 30 units in 3
+// slices, ran 5 % slower split; the 7680-wide down projection, 120 units
+// in 4, 10 % faster)
 static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
-  const int units = (int)units_of(K);
   const int total = (int)(((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN));
-  SplitPlan p = {total, 0, 1, units};
-  const int tail = total % kCUs;
-  if (tail == 0 || 2 * tail > kCUs) return p;
-  const int s = min(min(kCUs / tail, kMaxSplits), units / 2);
-  // worth it only if the round gets shorter by more than the slice and
-  // fixup launches cost: measured, the fixup alone takes about as long as
-  // 15-20 raw units of a tile (the QKV shape, 30 units in 3 slices, ran
-  // 5 % slower split; the 7680-wide down projection, 120 units in 4, 10 %
-  // faster)
-  if (s < 2 || units * (s - 1) / s < kSplitMinSaved) return p;
-  p.main_tiles = total - tail;
-  p.tail = tail;
-  p.split_units = (units + s - 1) / s;
-  p.splits = (units + p.split_units - 1) / p.split_units;   // no empty slice
-  return p;
+  return plan_split(total, (int)units_of(K), kCUs, kMaxSplits, kSplitMinSaved);
 }
 // the slices' partial sums
 static size_t split_ws_bytes(const SplitPlan& p) {

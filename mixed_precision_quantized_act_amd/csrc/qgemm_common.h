@@ -7,6 +7,7 @@
 
 #include "qact_device.h"
 #include "qact_internal.h"
+#include "tile_order.h"
 
 namespace qact {
 

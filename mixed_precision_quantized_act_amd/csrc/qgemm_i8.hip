@@ -183,7 +183,6 @@ struct I8Args {
 
 // the test-only epilogue: store H and L themselves
 constexpr int kEpiAcc = 100;
-enum { kWhole = 0, kSlice = 1, kFixup = 2 };
 
 template <int kEpi, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -193,27 +192,12 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
 
   // tile of this workgroup: XCD-aware order as in the fp16 kernel (each
   // XCD a contiguous range of logical tiles, grouped 8 tile-rows at a time)
-  const int bid = (int)blockIdx.x;
-  int logical, slice = 0, u_begin = 0, u_count = g.units;
-  if constexpr (kMode == kWhole) {
-    const int per_xcd = (g.main_tiles + 7) / 8;
-    logical = (bid & 7) * per_xcd + (bid >> 3);
-    if (logical >= g.main_tiles) return;
-  } else if constexpr (kMode == kSlice) {
-    logical = g.main_tiles + bid / g.splits;
-    slice = bid % g.splits;
-    u_begin = slice * g.split_units;
-    u_count = min(g.units - u_begin, g.split_units);
-  } else {
-    logical = g.main_tiles + bid;
-  }
-  constexpr int kGroup = 8;
-  const int group = logical / (kGroup * g.nt);
-  const int first_m = group * kGroup;
-  const int gsz = min(g.mt - first_m, kGroup);
-  const int in_group = logical - group * kGroup * g.nt;
-  const int tm = first_m + in_group % gsz;
-  const int tn = in_group / gsz;
+  TileWork tw;
+  if (!tile_work(kMode, (int)blockIdx.x, g.main_tiles, g.splits, g.split_units, g.units, tw))
+    return;
+  const int logical = tw.logical, slice = tw.slice, u_begin = tw.u_begin, u_count = tw.u_count;
+  int tm, tn;
+  tile_coords(logical, g.mt, g.nt, 8, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -474,22 +458,9 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
 
 namespace {
 
-struct SplitPlan {
-  int main_tiles, tail, splits, split_units;
-};
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
-  const int units = (int)units_of(K);
   const int total = (int)(((M + kTileM - 1) / kTileM) * ntiles_of(N));
-  SplitPlan p = {total, 0, 1, units};
-  const int tail = total % kCUs;
-  if (tail == 0 || 2 * tail > kCUs) return p;
-  const int s = min(min(kCUs / tail, kMaxSplits), units / 2);
-  if (s < 2 || units * (s - 1) / s < kSplitMinSaved) return p;
-  p.main_tiles = total - tail;
-  p.tail = tail;
-  p.split_units = (units + s - 1) / s;
-  p.splits = (units + p.split_units - 1) / p.split_units;
-  return p;
+  return plan_split(total, (int)units_of(K), kCUs, kMaxSplits, kSplitMinSaved);
 }
 
 hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
