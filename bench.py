@@ -660,6 +660,46 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     return res
 
 
+def design_ab(qa, torch, np, dev, stream, iters=2000, blocks=1024, reps=5):
+    """The compute stage of the NVFP4 linear's designs on register-resident
+    operands (qa_test_stage_ab): 0 = exact fp16 expansion with the group
+    scales, fp16 MFMA accumulating (the library's); 1 = design S, codes as
+    fp8, one fp8 MFMA per 16-element group from zero and a rescale by
+    s_a s_w per output; 2 = S with the activation scale folded into fp16
+    operands and a rescale by s_w.  Rates in MAC-equivalent TFLOP/s (2 x
+    multiply-accumulates of the tile per second), median of `reps`."""
+    rng = np.random.default_rng(7)
+    blk = rng.integers(0, 1 << 32, (1024, 64), dtype=np.uint64).astype(np.uint32)
+    blk[:, 12:14] = np.float32(1.5).view(np.uint32)               # scales: finite values
+    blk[:, 16:64] = np.float32(0.75).view(np.uint32)
+    for w in range(4, 12):                                         # fp8 bytes without NaN codes
+        blk[:, w] &= 0x77777777
+    blk[:, 0:4] &= 0x77777777
+    blk[:, 8:16] = 0x38
+    inp = torch.from_numpy(blk.view(np.int32).copy()).to(dev)
+    out = torch.empty((1024, 256), dtype=torch.float32, device=dev)
+    res = {}
+    for design, mfmas in ((0, 16), (1, 8), (2, 8)):
+        qa._lib.stage_ab(design, 10, blocks, inp, out, stream=stream)
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            qa._lib.stage_ab(design, iters, blocks, inp, out, stream=stream)
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts))
+        macs = blocks * 4 * iters * mfmas * 32 * 32 * 16
+        res[("D_fp16_exact", "S_fp8_rescale", "S_fp16_rescale")[design]] = {
+            "ms": round(ms, 3), "TFLOP/s": round(2 * macs / (ms * 1e-3) / 1e12, 1)}
+    best = max(res, key=lambda k: res[k]["TFLOP/s"])
+    res["winner"] = best
+    res["note"] = ("compute stage only, operands in registers; memory traffic is the same "
+                   "4-bit codes and E4M3 scales in every design")
+    return res
+
+
 def sections(args, qa, torch, np, hip, dev, stream, to_dev, xd, xod, dpd, wq, wsc, wts, w8,
              aq, asc, ats, qws, a8, s8, y4, y8, ws4, ws8, dnew, applied, s4, s2, rws, M, N, K):
     """The cold bandwidth kernels, the INT8 kernel A/B and the fused FFN
@@ -938,8 +978,9 @@ def main():
                 hip.destroy(b)
     avg = {k: float(np.mean(v)) for k, v in ev.items() if v}
 
-    cold = int8_ab = ffn_fused = None
+    cold = int8_ab = ffn_fused = design = None
     if not args.step_only:
+        design = design_ab(qa, torch, np, dev, stream)
         cold, int8_ab, ffn_fused = sections(args, qa, torch, np, hip, dev, stream, to_dev, xd, xod,
                                             dpd, wq, wsc, wts, w8, aq, asc, ats, qws, a8, s8,
                                             y4, y8, ws4, ws8, dnew, applied, s4, s2, rws, M, N, K)
@@ -1050,6 +1091,7 @@ def main():
         "int8_kernel_ab": int8_ab,
         "cold": cold,
         "ffn_up_fused_nvfp4_output": ffn_fused,
+        "nvfp4_design_ab": design,
         "stack_cogvideox2b_shape": stack,
         "per_layer_qlinear_cogvideox2b_shape": layers2b,
         "ffn_student_t": ffn3,

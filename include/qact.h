@@ -426,6 +426,22 @@ int qa_set_gate(const uint8_t* flags, uint32_t bits);
  * Outputs for NaN or infinite inputs (ops 0 and 2) are not specified. */
 int qa_test_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream);
 
+/* Test and benchmark only: the compute stage of three designs of the NVFP4
+ * linear (6Bit-Diffusion, abstract: NVFP4 activations and weights, one E4M3
+ * scale per 16 elements) on register-resident operands, `iters` 16-element
+ * scale groups per wave, `blocks` workgroups of 256 lanes:
+ *   design 0  both operands expanded exactly to fp16 with their group
+ *             scales, fp16 MFMA accumulating across groups (the library's);
+ *   design 1  codes as fp8, one fp8 MFMA per group from zero, the partial
+ *             product rescaled by s_a s_w per output into float32 sums;
+ *   design 2  activations scaled into fp16, weight codes unscaled, fp16
+ *             MFMA per group from zero, rescaled by s_w per output.
+ * in: device u32 [1024][64] per-lane operands (layout in stage_ab.hip);
+ * out: device f32 [1024][256], lane (g % 1024)'s accumulators.  Lanes g and
+ * g + 1024 k read and write the same rows with the same values. */
+int qa_test_stage_ab(int design, int iters, int blocks, const uint32_t* in, float* out,
+                     hipStream_t stream);
+
 /* Profiling hook: while set, each qlinear_nvfp4 / qlinear_int8 call (also
  * inside qlinear) launches its main GEMM kernel with hipExtLaunchKernel so
  * that `before` and `after` take that dispatch's start and end timestamps

@@ -71,6 +71,7 @@ _SIGS = {
     "tdc_decide": (ctypes.c_int, [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_double, _P]),
     "qa_set_gemm_events": (ctypes.c_int, [_P, _P]),
     "qa_test_convert": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint32, _I64, _P, _P]),
+    "qa_test_stage_ab": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P, _P]),
     "qa_set_gate": (ctypes.c_int, [_P, ctypes.c_uint32]),
     "qa_decide_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_double, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -393,6 +394,14 @@ def convert_check(op, first, out, count=None, stream=None):
     the device tensor out (u8, or int16 for bf16)."""
     count = out.numel() if count is None else count
     _check("qa_test_convert", lib().qa_test_convert(op, first, count, _ptr(out), _stream(stream)))
+
+
+def stage_ab(design, iters, blocks, inp, out, stream=None):
+    """Test/benchmark only: the compute stage of NVFP4 GEMM design 0, 1 or 2
+    (qa_test_stage_ab) on the per-lane operands in `inp` (int32 [1024, 64])
+    into `out` (float32 [1024, 256])."""
+    _check("qa_test_stage_ab", lib().qa_test_stage_ab(design, iters, blocks, _ptr(inp), _ptr(out),
+                                                      _stream(stream)))
 
 
 def set_gemm_events(before, after):

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libqact.so")
 ROOT = os.path.dirname(HERE)
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["act_quant.hip", "qgemm.hip", "qgemm_i8.hip", "tdc.hip", "noalloc.hip", "convert_check.hip", "abi.cpp"]
+SOURCES = ["act_quant.hip", "qgemm.hip", "qgemm_i8.hip", "tdc.hip", "noalloc.hip", "convert_check.hip", "stage_ab.hip", "abi.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

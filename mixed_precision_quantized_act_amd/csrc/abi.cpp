@@ -530,6 +530,15 @@ int qa_test_convert(int op, uint32_t first, int64_t count, void* out, hipStream_
   return hip_status(launch_convert(op, first, count, out, stream));
 }
 
+int qa_test_stage_ab(int design, int iters, int blocks, const uint32_t* in, float* out,
+                     hipStream_t stream) {
+  if (design < 0 || design > 2 || iters < 0 || blocks < 1 || blocks > 65535 || !in || !out)
+    return QA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(in) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return QA_EALIGN;
+  return hip_status(launch_stage_ab(design, iters, blocks, in, out, stream));
+}
+
 int qa_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr)) return QA_EINVAL;
   set_gemm_events(before, after);

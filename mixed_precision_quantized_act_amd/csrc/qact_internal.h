@@ -51,6 +51,10 @@ hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ld
 // ---- test-only element conversions (convert_check.hip)
 hipError_t launch_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream);
 
+// ---- test/benchmark-only compute stages of three NVFP4 GEMM designs (stage_ab.hip)
+hipError_t launch_stage_ab(int design, int iters, int blocks, const uint32_t* in, float* out,
+                           hipStream_t stream);
+
 // ---- profiling hook: events recorded around each main GEMM kernel
 void set_gemm_events(hipEvent_t before, hipEvent_t after);
 
