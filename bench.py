@@ -532,10 +532,12 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
 
     outs = None
 
-    def run_device(tau, delta, graph):
+    def run_device(tau, delta, graph, routed=True):
         """DMPQ + TDC with the decisions made on the device
         (qa.decide_step) and every path enqueued under its gate: no host
-        sync inside a step; graph: one step captured as a HIP graph and
+        sync inside a step (routed: the activation quantization and the Delta
+        ring calls take their format or slot from the gate byte in one launch
+        each; otherwise one gated launch per choice); graph: one step captured as a HIP graph and
         replayed.  Mean ms/step of steps 2.. (one sync around them)."""
         nonlocal outs
         if outs is None:
@@ -558,10 +560,39 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                 b.zero_()
 
         def gated_linear(j, l, x, ldx, y, gelu, stream, amax_out=None, amax_ws=None):
-            for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
-                with qa.gate(lin[l * J + j:], bit):
-                    linear(fmt, x, ldx, layers[l][j], y, gelu, stream=stream, amax_out=amax_out,
-                           amax_ws=amax_ws)
+            flag = lin[l * J + j:]
+            if not routed:
+                for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
+                    with qa.gate(flag, bit):
+                        linear(fmt, x, ldx, layers[l][j], y, gelu, stream=stream,
+                               amax_out=amax_out, amax_ws=amax_ws)
+                return
+            q, sc, ts, N, K, w8 = layers[l][j]
+            xv = torch.as_strided(x, (M, K), (ldx, 1))
+            aq4 = a4[0].view(-1)[: M * K // 2].view(M, K // 2)
+            as4 = a4[1].view(-1)[: M * K // 16].view(M, K // 16)
+            aq8 = a8[0].view(-1)[: M * K].view(M, K)
+            if amax_ws is not None:
+                qa.act_quant_routed(flag, i16(xv), aq4, as4, a4[2], qa.AMAX_GIVEN, amax_ws, aq8,
+                                    a8[1], M=M, K=K, ldx=ldx, stream=stream)
+            else:
+                qa.act_quant_routed(flag, i16(xv), aq4, as4, a4[2], 0, qws, aq8, a8[1], M=M, K=K,
+                                    ldx=ldx, stream=stream)
+            epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+            with qa.gate(flag, qa.ROUTE_NVFP4):
+                if amax_out is not None:
+                    qa.qlinear_nvfp4_amax(aq4, as4, a4[2], q, sc, ts, y, amax_out, M, N, K,
+                                          epi=epi, ws=gws, stream=stream)
+                else:
+                    qa.qlinear_nvfp4(aq4, as4, a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=gws,
+                                     stream=stream)
+            with qa.gate(flag, qa.ROUTE_INT8):
+                if amax_out is not None:
+                    qa.qlinear_int8_amax(aq8, a8[1], q, sc, ts, y, amax_out, M, N, K, epi=epi,
+                                         ws=gws, stream=stream, w8=w8)
+                else:
+                    qa.qlinear_int8(aq8, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws,
+                                    stream=stream, w8=w8)
 
         def step(stream):
             qa.decide_step(sums, alpha_d, beta_d, tau, delta, L, J, t_ctr, bstate, d_dev, blk,
@@ -571,10 +602,14 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             for l in range(L):
                 out = outs[l]
                 r0, r1 = ring[l]
-                for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
-                    with qa.gate(blk[l:], bit):
-                        qa.tdc_apply_amax(i16(cur), i16(slot), i16(out), sl_w(l + 1, 0),
-                                          sums[l, :2], rws, stream=stream)
+                if routed:
+                    qa.tdc_apply_ring(blk[l:], i16(cur), i16(r0), i16(r1), i16(out), sums[l, :2],
+                                      rws, out_amax=sl_w(l + 1, 0), stream=stream)
+                else:
+                    for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
+                        with qa.gate(blk[l:], bit):
+                            qa.tdc_apply_amax(i16(cur), i16(slot), i16(out), sl_w(l + 1, 0),
+                                              sums[l, :2], rws, stream=stream)
                 gated_linear(0, l, cur, H, qkv, False, stream,
                              amax_ws=sl_ws(l, 0) if l else None)
                 gated_linear(1, l, qkv.view(-1)[2 * H:], 3 * H, o, False, stream)
@@ -587,10 +622,14 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
                 with qa.gate(blk[l:], qa.BLK_RUN0 | qa.BLK_RUN1):
                     qa.tdc_apply_amax(i16(x1), i16(dd), i16(out), sl_w(l + 1, 0), None, rws,
                                       stream=stream)
-                for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
-                    with qa.gate(blk[l:], bit):
-                        qa.tdc_update(i16(cur), i16(out), i16(prev), i16(nxt), sums[l], rws,
-                                      stream=stream)
+                if routed:
+                    qa.tdc_update_ring(blk[l:], i16(cur), i16(out), i16(r0), i16(r1), sums[l], rws,
+                                       stream=stream)
+                else:
+                    for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
+                        with qa.gate(blk[l:], bit):
+                            qa.tdc_update(i16(cur), i16(out), i16(prev), i16(nxt), sums[l], rws,
+                                          stream=stream)
                 cur = out
 
         g = None
@@ -621,7 +660,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
         del g
         return {"ms_per_step": round(1e3 * dt / (steps - 2), 2), "delta": delta,
                 "skipped_blocks": int(skip_acc.sum().item()), "blocks_run": L * steps,
-                "decisions": "device", "graph": graph}
+                "decisions": "device", "graph": graph,
+                "launches": "routed (one per format/slot choice)" if routed
+                            else "one gated launch per choice"}
 
     res = {m: run(m) for m in ("w4a8", "w4a4", "dmpq", "full") if m in modes}
     # the synthetic trajectory's block updates change by d ~ d_median from
@@ -634,6 +675,8 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
         tau_d = res["dmpq"]["tau"]
         res["full_device"] = run_device(tau_d, delta, graph=False)
         res["full_device_graph"] = run_device(tau_d, delta, graph=True)
+        res["full_device_graph_per_choice_gates"] = run_device(tau_d, delta, graph=True,
+                                                               routed=False)
         if "full_delta_at_median_d" in res:
             dm = res["dmpq"]["d_median"]
             res["full_delta_at_median_d_device"] = run_device(tau_d, dm, graph=False)

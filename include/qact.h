@@ -106,6 +106,21 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
               void* q, void* scales, float* tscale, uint32_t flags,
               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* act_quant_routed: act_quant in the format that the device byte *route
+ * selects, in one launch, for a timestep enqueued (or captured in a graph)
+ * before its decisions are known (6Bit-Diffusion, Fig. 2 caption: each
+ * linear's activation format is chosen per timestep).  *route is a linear
+ * gate byte of qa_decide_step: (*route & 1) NVFP4 into (q4, s4, *ts4) with
+ * flags4 and ws4 as for act_quant (QA_TSCALE_GIVEN or QA_AMAX_GIVEN: the
+ * encoder alone; neither: a tensor-max launch first, which also runs only
+ * for NVFP4); (*route & 2) INT8 into (q8, s8); 0: nothing.  The outputs of
+ * the format not chosen are left as they were.  Arguments as for act_quant
+ * (both formats' buffers required); the outputs overlap neither each other
+ * nor x. */
+int act_quant_routed(const uint8_t* route, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     uint8_t* q4, uint8_t* s4, float* ts4, uint32_t flags4, void* ws4,
+                     size_t ws4_bytes, int8_t* q8, float* s8, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * qlinear_nvfp4_q / qlinear_int8_q: the same linears with the output
  * quantized to NVFP4 in the GEMM epilogue, for a consumer linear that
@@ -308,6 +323,26 @@ int tdc_apply_amax(const uint16_t* in, const uint16_t* delta, uint16_t* out, int
                    double* sums2, uint32_t* out_amax, void* ws, size_t ws_bytes,
                    hipStream_t stream);
 
+/* tdc_update_ring / tdc_apply_ring: tdc_update / tdc_apply on a block's
+ * Delta ring (two bf16 [n] slots), the slot chosen on the device from the
+ * block's gate byte *blk of qa_decide_step (abstract and Fig. 2 caption:
+ * the cached residual of a block is refreshed when it runs and reused when
+ * it is skipped):
+ *   tdc_update_ring: QA_BLK_RUN0 (1) reads Delta_prev from ring0 and writes
+ *     Delta_new to ring1; QA_BLK_RUN1 (2) reads ring1, writes ring0;
+ *   tdc_apply_ring: QA_BLK_SKIP0 (4) applies ring0, QA_BLK_SKIP1 (8) ring1,
+ *     with the |max| of the outputs into out_amax (nullable) as
+ *     tdc_apply_amax;
+ * any other byte: nothing, outputs and sums left as they were.  One launch
+ * (plus the sums' finalize) instead of one per slot.  The slots must not
+ * overlap each other or the call's other buffers. */
+int tdc_update_ring(const uint8_t* blk, const uint16_t* in, const uint16_t* out, uint16_t* ring0,
+                    uint16_t* ring1, int64_t n, double* sums4, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+int tdc_apply_ring(const uint8_t* blk, const uint16_t* in, const uint16_t* ring0,
+                   const uint16_t* ring1, uint16_t* out, int64_t n, double* sums2,
+                   uint32_t* out_amax, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* rel_err (Fig. 3 caption: E_rel, the layer-wise relative quantization
  * error at a timestep, to which the DMPQ predictor is fitted; read here as
  * the relative L2 error of the layer output against its bf16 computation):
@@ -405,6 +440,13 @@ int tdc_decide_cos(int t, const double* cos_prev, const uint8_t* computed_prev, 
  * and skip paths of each block, the Delta update for either ring slot),
  * each under its gate byte and bits.  Per thread; bits != 0 when flags is
  * set. */
+/* gate bytes written by qa_decide_step */
+#define QA_ROUTE_NVFP4 1u   /* lin_flags: the linear runs on NVFP4 activations */
+#define QA_ROUTE_INT8 2u    /* lin_flags: ... on INT8 activations */
+#define QA_BLK_RUN0 1u      /* blk_flags: compute, Delta ring slot last = 0 */
+#define QA_BLK_RUN1 2u      /* blk_flags: compute, last = 1 */
+#define QA_BLK_SKIP0 4u     /* blk_flags: skip, apply slot 0 */
+#define QA_BLK_SKIP1 8u     /* blk_flags: skip, apply slot 1 */
 int qa_decide_step(const double* sums, const float* alpha, const float* beta, double tau,
                    double delta, int L, int J, int* t_ctr, uint8_t* bstate, double* d_prev,
                    uint8_t* blk_flags, uint8_t* lin_flags, uint8_t* mask_out, uint8_t* skip_out,

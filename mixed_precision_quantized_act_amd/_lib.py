@@ -57,6 +57,10 @@ _SIGS = {
     "qlinear_layer_workspace": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
     "qlinear": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, ctypes.c_uint32, _P, _P, _P, _P, _I64,
                                _I64, _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
+    "act_quant_routed": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, ctypes.c_uint32, _P,
+                                        _SZ, _P, _P, _P]),
+    "tdc_update_ring": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "tdc_apply_ring": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "reduce_workspace": (_SZ, [_I64]),
     "block_gamma": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_update": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -261,6 +265,36 @@ def qlinear(fmt, x, x_ts, w_q, w_s, w_ts, y, M, N, K, bias=None, out=OUT_BF16, e
 
 
 # ------------------------------------------------------------- Gamma / TDC --
+
+def act_quant_routed(route, x, q4, s4, ts4, flags4, ws4, q8, s8, M=None, K=None, ldx=None,
+                     stream=None):
+    """act_quant in the format the device byte route[0] selects (1 NVFP4,
+    2 INT8, 0 nothing), one launch."""
+    M = x.shape[0] if M is None else M
+    K = x.shape[1] if K is None else K
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("act_quant_routed", lib().act_quant_routed(
+        _ptr(route), _ptr(x), M, K, ldx, _ptr(q4), _ptr(s4), _ptr(ts4), flags4, _ptr(ws4),
+        _nbytes(ws4), _ptr(q8), _ptr(s8), _stream(stream)))
+
+
+def tdc_update_ring(blk, x_in, x_out, ring0, ring1, sums4, ws, n=None, stream=None):
+    """tdc_update with the ring slot from the device byte blk[0]."""
+    n = x_in.numel() if n is None else n
+    _check("tdc_update_ring", lib().tdc_update_ring(
+        _ptr(blk), _ptr(x_in), _ptr(x_out), _ptr(ring0), _ptr(ring1), n, _ptr(sums4), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
+
+
+def tdc_apply_ring(blk, x_in, ring0, ring1, x_out, sums2=None, ws=None, out_amax=None, n=None,
+                   stream=None):
+    """tdc_apply (and tdc_apply_amax with out_amax) of the ring slot that
+    the device byte blk[0] selects."""
+    n = x_in.numel() if n is None else n
+    _check("tdc_apply_ring", lib().tdc_apply_ring(
+        _ptr(blk), _ptr(x_in), _ptr(ring0), _ptr(ring1), _ptr(x_out), n, _ptr(sums2),
+        _ptr(out_amax), _ptr(ws), _nbytes(ws), _stream(stream)))
+
 
 def reduce_workspace(n):
     return lib().reduce_workspace(n)

@@ -14,6 +14,11 @@
 
 using namespace qact;
 
+static_assert(kRouteNvfp4 == QA_ROUTE_NVFP4 && kRouteInt8 == QA_ROUTE_INT8, "gate bytes");
+static_assert(kBlkRun0 == QA_BLK_RUN0 && kBlkRun1 == QA_BLK_RUN1 && kBlkSkip0 == QA_BLK_SKIP0 &&
+                  kBlkSkip1 == QA_BLK_SKIP1,
+              "gate bytes");
+
 namespace {
 
 // Size limits.  The GEMM kernels address a tile's operand rows (at most 256
@@ -127,6 +132,34 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   return hip_status(launch_nvfp4_quant(x, M, K, ldx, static_cast<uint8_t*>(q),
                                        static_cast<uint8_t*>(scales), tscale, given, amax_given,
                                        ws, stream));
+}
+
+int act_quant_routed(const uint8_t* route, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     uint8_t* q4, uint8_t* s4, float* ts4, uint32_t flags4, void* ws4,
+                     size_t ws4_bytes, int8_t* q8, float* s8, hipStream_t stream) {
+  if (!route || !x || !q4 || !s4 || !ts4 || !q8 || !s8) return QA_EINVAL;
+  if (int s = check_mk(M, K)) return s;
+  if (ldx < K || ldx % 8) return QA_ESHAPE;
+  if (!aligned16(x) || !aligned16(q4) || !aligned16(q8)) return QA_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(ts4) & 3u) || (reinterpret_cast<uintptr_t>(s8) & 3u))
+    return QA_EALIGN;
+  if (flags4 & ~(QA_TSCALE_GIVEN | QA_AMAX_GIVEN)) return QA_EINVAL;
+  if ((flags4 & QA_TSCALE_GIVEN) && (flags4 & QA_AMAX_GIVEN)) return QA_EINVAL;
+  const bool given = (flags4 & QA_TSCALE_GIVEN) != 0;
+  const bool amax_given = (flags4 & QA_AMAX_GIVEN) != 0;
+  if (!given && (!ws4 || ws4_bytes < nvfp4_quant_ws_bytes(M, K))) return QA_EWORKSPACE;
+  if (!given && (reinterpret_cast<uintptr_t>(ws4) & 3u)) return QA_EALIGN;
+  const size_t xbytes = M ? (size_t)((M - 1) * ldx + K) * 2 : 0;
+  const void* outs[4] = {q4, s4, q8, s8};
+  const size_t ob[4] = {(size_t)(M * K / 2), (size_t)(M * K / 16), (size_t)(M * K), (size_t)M * 4};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(x, xbytes, outs[i], ob[i])) return QA_EALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], ob[i], outs[j], ob[j])) return QA_EALIAS;
+  }
+  if (M == 0) return QA_OK;
+  return hip_status(launch_act_quant_routed(route, x, M, K, ldx, q4, s4, ts4, given, amax_given,
+                                            ws4, q8, s8, stream));
 }
 
 // -------------------------------------------------------------- qlinear --
@@ -502,6 +535,53 @@ int tdc_apply_amax(const uint16_t* in, const uint16_t* delta, uint16_t* out, int
       (sums2 && overlap(out_amax, ab, sums2, 16)))
     return QA_EALIAS;
   return hip_status(launch_tdc(5, in, delta, nullptr, out, n, sums2, ws, stream, out_amax));
+}
+
+// the Delta ring of one block: two bf16 [n] slots, each 16-byte aligned,
+// overlapping neither each other nor the other buffers of the call
+static int check_ring(const uint8_t* blk, const uint16_t* ring0, const uint16_t* ring1,
+                      const void* in, const void* other, int64_t n, const void* ws,
+                      size_t ws_bytes) {
+  if (!blk || !ring0 || !ring1) return QA_EINVAL;
+  if (!aligned16(ring0) || !aligned16(ring1)) return QA_EALIGN;
+  const size_t b = (size_t)n * 2;
+  if (overlap(ring0, b, ring1, b)) return QA_EALIAS;
+  for (const void* r : {static_cast<const void*>(ring0), static_cast<const void*>(ring1)})
+    if (overlap(r, b, in, b) || overlap(r, b, other, b) || overlap(r, b, ws, ws_bytes))
+      return QA_EALIAS;
+  return QA_OK;
+}
+
+int tdc_update_ring(const uint8_t* blk, const uint16_t* in, const uint16_t* out, uint16_t* ring0,
+                    uint16_t* ring1, int64_t n, double* sums4, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!sums4) return QA_EINVAL;
+  if (int s = check_stream(in, out, n, ws, ws_bytes, true)) return s;
+  if (int s = check_ring(blk, ring0, ring1, in, out, n, ws, ws_bytes)) return s;
+  const RingRoute rt = {blk, kBlkRun0, kBlkRun1, out, ring1, ring0};
+  return hip_status(launch_tdc(1, in, out, ring0, ring1, n, sums4, ws, stream, nullptr, &rt));
+}
+
+int tdc_apply_ring(const uint8_t* blk, const uint16_t* in, const uint16_t* ring0,
+                   const uint16_t* ring1, uint16_t* out, int64_t n, double* sums2,
+                   uint32_t* out_amax, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!out) return QA_EINVAL;
+  if (int s = check_stream(in, ring0, n, ws, ws_bytes, sums2 != nullptr)) return s;
+  if (!aligned16(out)) return QA_EALIGN;
+  const size_t b = (size_t)n * 2;
+  if (out != in && overlap(out, b, in, b)) return QA_EALIAS;
+  if (int s = check_ring(blk, ring0, ring1, in, out, n, ws, ws_bytes)) return s;
+  if (out_amax) {
+    if (reinterpret_cast<uintptr_t>(out_amax) & 3u) return QA_EALIGN;
+    const size_t ab = kAmaxSlots * 4;
+    if (overlap(out_amax, ab, out, b) || overlap(out_amax, ab, in, b) ||
+        overlap(out_amax, ab, ring0, b) || overlap(out_amax, ab, ring1, b) ||
+        overlap(out_amax, ab, ws, ws_bytes) || (sums2 && overlap(out_amax, ab, sums2, 16)))
+      return QA_EALIAS;
+  }
+  const RingRoute rt = {blk, kBlkSkip0, kBlkSkip1, ring1, nullptr, out};
+  return hip_status(launch_tdc(out_amax ? 5 : 2, in, ring0, nullptr, out, n, sums2, ws, stream,
+                               out_amax, &rt));
 }
 
 int rel_err(const uint16_t* y_q, const uint16_t* y_ref, int64_t n, double* sums2, void* ws,

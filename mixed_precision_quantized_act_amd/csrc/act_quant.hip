@@ -44,8 +44,8 @@ __device__ __forceinline__ void block_max_to(float v, float* dst) {
 template <bool CONTIG>
 __global__ void __launch_bounds__(256)
 nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                  float* __restrict__ partial, Gate gate) {
-  if (gated_off(gate)) return;
+                  float* __restrict__ partial, Gate gate, Gate route) {
+  if (gated_off(gate) || gated_off(route)) return;
   uint32_t mx = 0;
   if (CONTIG) {
     const int64_t nvec = M * K / 8;
@@ -78,19 +78,20 @@ nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t 
 // one float32 tensor scale).  K % 16 == 0, so a group is the even vector v and v + 1, held
 // by lanes 2j and 2j+1.  Outputs are indexed by v alone: code word v of
 // the [M][K/2] code array and scale byte v / 2 of the [M][K/16] scales.
+// (run by workgroup `bid` of `nblk`)
 template <int U>
-__global__ void __launch_bounds__(256)
-nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                        uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-                        float* __restrict__ tscale, const float* __restrict__ partial,
-                        int nparts, int given, Gate gate) {
-  if (gated_off(gate)) return;
+__device__ __forceinline__ void nvfp4_encode_body(const uint16_t* __restrict__ x, int64_t M,
+                                                  int64_t K, int64_t ldx, uint8_t* __restrict__ q,
+                                                  uint8_t* __restrict__ scales,
+                                                  float* __restrict__ tscale,
+                                                  const float* __restrict__ partial, int nparts,
+                                                  int given, int bid, int nblk) {
   const int64_t vpr = K / 8;                               // vectors per row
   const int64_t nvec = M * vpr;
   const bool contig = ldx == K;
   const bool small = nvec <= 0xFFFFFFFFll;
-  const int64_t sweep = (int64_t)gridDim.x * 256 * U;
-  const int64_t start = (int64_t)blockIdx.x * 256 * U + threadIdx.x;
+  const int64_t sweep = (int64_t)nblk * 256 * U;
+  const int64_t start = (int64_t)bid * 256 * U + threadIdx.x;
   auto load = [&](int64_t v0, u32x4 (&w)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -126,7 +127,7 @@ nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, in
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     s_t = amax / 2688.0f;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = s_t;
+    if (bid == 0 && threadIdx.x == 0) *tscale = s_t;
   }
   const float g = recip0(6.0f * s_t);
   uint32_t* const q32 = reinterpret_cast<uint32_t*>(q);
@@ -151,6 +152,17 @@ nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, in
   }
 }
 
+template <int U>
+__global__ void __launch_bounds__(256)
+nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                        uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                        float* __restrict__ tscale, const float* __restrict__ partial,
+                        int nparts, int given, Gate gate) {
+  if (gated_off(gate)) return;
+  nvfp4_encode_body<U>(x, M, K, ldx, q, scales, tscale, partial, nparts, given, (int)blockIdx.x,
+                       (int)gridDim.x);
+}
+
 // ----------------------------------------------------------------- INT8 --
 
 __device__ __forceinline__ u32x2 int8_pack8(u32x4 a, float inv) {
@@ -169,13 +181,10 @@ __device__ __forceinline__ u32x2 int8_pack8(u32x4 a, float inv) {
 // per lane) is held in registers between the row max and the encode, so
 // it is read once; VPL == 0: any K, the row is read twice.
 template <int VPL>
-__global__ void __launch_bounds__(256)
-int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                   int8_t* __restrict__ q, float* __restrict__ scale, Gate gate) {
-  if (gated_off(gate)) return;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void int8_encode_row(const uint16_t* __restrict__ x, int64_t row,
+                                                int64_t K, int64_t ldx, int8_t* __restrict__ q,
+                                                float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  if (row >= M) return;
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * ldx);
   u32x2* qr = reinterpret_cast<u32x2*>(q + row * K);
   const int64_t nvec = K / 8;
@@ -206,6 +215,44 @@ int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t
   }
 }
 
+template <int VPL>
+__global__ void __launch_bounds__(256)
+int8_encode_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                   int8_t* __restrict__ q, float* __restrict__ scale, Gate gate) {
+  if (gated_off(gate)) return;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row < M) int8_encode_row<VPL>(x, row, K, ldx, q, scale);
+}
+
+// ---------------------------------------------------------------- routed --
+
+// One launch for either format, the format read from the device byte
+// *route (kRouteNvfp4: the NVFP4 encoder on its first nvfp4_blocks
+// workgroups, with a given tensor scale or the partial maxima in `partial`;
+// kRouteInt8: every workgroup takes token rows 4 b + wave, 4 (b + grid) +
+// wave, ...; neither: nothing).  6Bit-Diffusion, Fig. 2 caption: the format
+// of each linear's activations is chosen per timestep.
+template <int U, int VPL>
+__global__ void __launch_bounds__(256)
+act_quant_routed_kernel(const uint8_t* __restrict__ route, const uint16_t* __restrict__ x,
+                        int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q4,
+                        uint8_t* __restrict__ s4, float* __restrict__ ts4,
+                        const float* __restrict__ partial, int nparts, int given,
+                        int nvfp4_blocks, int8_t* __restrict__ q8, float* __restrict__ s8,
+                        Gate gate) {
+  if (gated_off(gate)) return;
+  const uint32_t r = *route;
+  if (r & kRouteNvfp4) {
+    if ((int)blockIdx.x < nvfp4_blocks)
+      nvfp4_encode_body<U>(x, M, K, ldx, q4, s4, ts4, partial, nparts, given, (int)blockIdx.x,
+                           nvfp4_blocks);
+  } else if (r & kRouteInt8) {
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M;
+         row += (int64_t)gridDim.x * 4)
+      int8_encode_row<VPL>(x, row, K, ldx, q8, s8);
+  }
+}
+
 // ----------------------------------------------------------------- host --
 
 static constexpr int kAmaxBlocks = 1024;
@@ -232,10 +279,10 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
     nblk = (int)(work < kAmaxBlocks ? (work < 1 ? 1 : work) : kAmaxBlocks);
     if (contig)
       hipLaunchKernelGGL(nvfp4_amax_kernel<true>, dim3(nblk), dim3(256), 0, stream, x, M, K,
-                         ldx, partial, gt);
+                         ldx, partial, gt, Gate{nullptr, 0u});
     else
       hipLaunchKernelGGL(nvfp4_amax_kernel<false>, dim3(nblk), dim3(256), 0, stream, x, M, K,
-                         ldx, partial, gt);
+                         ldx, partial, gt, Gate{nullptr, 0u});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -264,6 +311,55 @@ hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ld
     hipLaunchKernelGGL(int8_encode_kernel<16>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
   else
     hipLaunchKernelGGL(int8_encode_kernel<0>, g, t, 0, stream, x, M, K, ldx, q, scale, gt);
+  return hipGetLastError();
+}
+
+// the INT8 rows per wave held in registers: 16-byte vectors per lane
+static int int8_vpl(int64_t K) {
+  const int64_t vpl = (K / 8 + 63) / 64;
+  return vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : vpl <= 16 ? 16 : 0;
+}
+
+hipError_t launch_act_quant_routed(const uint8_t* route, const uint16_t* x, int64_t M, int64_t K,
+                                   int64_t ldx, uint8_t* q4, uint8_t* s4, float* ts4, bool given,
+                                   bool amax_given, void* ws, int8_t* q8, float* s8,
+                                   hipStream_t stream) {
+  const Gate gt = current_gate();
+  float* partial = static_cast<float*>(ws);
+  int nblk = kAmaxSlots;
+  if (!given && !amax_given) {
+    // the tensor-max pass, run only when the route byte selects NVFP4
+    const Gate rg = {route, kRouteNvfp4};
+    const bool contig = ldx == K;
+    const int64_t work = contig ? (M * K / 8 + 256 * kUnroll - 1) / (256 * kUnroll) : M;
+    nblk = (int)(work < kAmaxBlocks ? (work < 1 ? 1 : work) : kAmaxBlocks);
+    if (contig)
+      hipLaunchKernelGGL(nvfp4_amax_kernel<true>, dim3(nblk), dim3(256), 0, stream, x, M, K, ldx,
+                         partial, gt, rg);
+    else
+      hipLaunchKernelGGL(nvfp4_amax_kernel<false>, dim3(nblk), dim3(256), 0, stream, x, M, K,
+                         ldx, partial, gt, rg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int64_t eblk = (M * (K / 8) + 256 * kEncU - 1) / (256 * kEncU);
+  if (eblk > kEncBlocks) eblk = kEncBlocks;
+  if (eblk < 1) eblk = 1;
+  const int64_t rows_blk = (M + 3) / 4;
+  const int64_t grid = rows_blk > eblk ? (rows_blk < 65535 ? rows_blk : 65535) : eblk;
+  const dim3 g((unsigned)grid), t(256);
+#define QACT_ROUTED(V)                                                                          \
+  hipLaunchKernelGGL((act_quant_routed_kernel<kEncU, V>), g, t, 0, stream, route, x, M, K, ldx, \
+                     q4, s4, ts4, partial, nblk, given ? 1 : 0, (int)eblk, q8, s8, gt)
+  switch (int8_vpl(K)) {
+    case 1: QACT_ROUTED(1); break;
+    case 2: QACT_ROUTED(2); break;
+    case 4: QACT_ROUTED(4); break;
+    case 8: QACT_ROUTED(8); break;
+    case 16: QACT_ROUTED(16); break;
+    default: QACT_ROUTED(0); break;
+  }
+#undef QACT_ROUTED
   return hipGetLastError();
 }
 

@@ -47,6 +47,13 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
                               bool amax_given, void* ws, hipStream_t stream);
 hipError_t launch_int8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                              float* scale, hipStream_t stream);
+// both formats in one launch, the format read from the device byte *route
+// (kRouteNvfp4 / kRouteInt8; the tensor-max pass, when needed, is a second
+// launch that runs only for kRouteNvfp4)
+hipError_t launch_act_quant_routed(const uint8_t* route, const uint16_t* x, int64_t M, int64_t K,
+                                   int64_t ldx, uint8_t* q4, uint8_t* s4, float* ts4, bool given,
+                                   bool amax_given, void* ws, int8_t* q8, float* s8,
+                                   hipStream_t stream);
 
 // ---- test-only element conversions (convert_check.hip)
 hipError_t launch_convert(int op, uint32_t first, int64_t count, void* out, hipStream_t stream);
@@ -111,10 +118,20 @@ int int8_linear_status(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
                        int64_t N, int64_t K, const void* y, int64_t ldy, qa_out out, qa_epi epi);
 
 size_t reduce_ws_bytes(int64_t n);
+// Operands chosen on the device from the byte *sel: the call's own (b,
+// delta_prev, dst) when (*sel & bits_a), these when (*sel & bits_b), no work
+// otherwise (the Delta ring slot of a block, from qa_decide_step).
+struct RingRoute {
+  const uint8_t* sel;
+  uint32_t bits_a, bits_b;
+  const uint16_t* b_alt;
+  const uint16_t* prev_alt;
+  uint16_t* dst_alt;
+};
 // mode 0: block_gamma, 1: tdc_update, 2: tdc_apply, 3: rel_err, 4: delta_cosine,
 // 5: tdc_apply that also max-combines |out| into *amax_out
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* delta_prev,
                       uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream,
-                      uint32_t* amax_out = nullptr);
+                      uint32_t* amax_out = nullptr, const RingRoute* route = nullptr);
 
 }  // namespace qact

@@ -85,13 +85,30 @@ __device__ __forceinline__ uint32_t tdc_pair(uint32_t xi, uint32_t bi, uint32_t 
   return dn;
 }
 
+// The operand set a kernel takes from a device byte (ring slot of the
+// Delta cache): the primary pointers when (*sel & bits_a), the alternates
+// when (*sel & bits_b), nothing otherwise; sel == nullptr: the primary ones.
+__device__ __forceinline__ bool pick_route(const RingRoute& rt, const uint16_t*& b,
+                                           const uint16_t*& prev, uint16_t*& dst) {
+  if (!rt.sel) return true;
+  const uint32_t v = *rt.sel;
+  if (v & rt.bits_a) return true;
+  if (v & rt.bits_b) {
+    b = rt.b_alt;
+    prev = rt.prev_alt;
+    dst = rt.dst_alt;
+    return true;
+  }
+  return false;
+}
+
 template <int MODE, bool PREV>
 __global__ void __launch_bounds__(kThreads)
-tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
-           const uint16_t* __restrict__ prev, uint16_t* dst, int64_t n,
+tdc_kernel(const uint16_t* in, const uint16_t* b, const uint16_t* prev, uint16_t* dst, int64_t n,
            double* __restrict__ partial, int want_sums, uint32_t* __restrict__ amax_out,
-           Gate gate) {
+           RingRoute rt, Gate gate) {
   if (gated_off(gate)) return;
+  if (!pick_route(rt, b, prev, dst)) return;
   constexpr bool kAmax = MODE == MODE_APPLY_AMAX;
   constexpr bool kWrites = MODE == MODE_UPDATE || MODE == MODE_APPLY || kAmax;
   uint32_t amx = 0;            // |max| of this thread's outputs (bf16 patterns)
@@ -167,8 +184,9 @@ tdc_kernel(const uint16_t* in, const uint16_t* __restrict__ b,
 // order.
 __global__ void __launch_bounds__(kThreads)
 tdc_finalize_kernel(const double* __restrict__ partial, int rows, int ncols,
-                    double* __restrict__ sums, Gate gate) {
+                    double* __restrict__ sums, RingRoute rt, Gate gate) {
   if (gated_off(gate)) return;
+  if (rt.sel && (*rt.sel & (rt.bits_a | rt.bits_b)) == 0u) return;
   __shared__ double red[4][kThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
@@ -267,8 +285,9 @@ size_t reduce_ws_bytes(int64_t) { return (size_t)kRedBlocks * 4 * sizeof(double)
 
 hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uint16_t* prev,
                       uint16_t* dst, int64_t n, double* sums, void* ws, hipStream_t stream,
-                      uint32_t* amax_out) {
+                      uint32_t* amax_out, const RingRoute* route) {
   const Gate gt = current_gate();
+  const RingRoute rt = route ? *route : RingRoute{nullptr, 0u, 0u, nullptr, nullptr, nullptr};
   const int64_t nvec = n / 8;
   int64_t nb = (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   // with sums, at most kRedBlocks partial rows; without, one sweep (measured
@@ -280,29 +299,30 @@ hipError_t launch_tdc(int mode, const uint16_t* in, const uint16_t* b, const uin
   const dim3 g((unsigned)nb), t(kThreads);
   if (mode == MODE_GAMMA)
     hipLaunchKernelGGL((tdc_kernel<MODE_GAMMA, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else if (mode == MODE_UPDATE && prev)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, true>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else if (mode == MODE_UPDATE)
     hipLaunchKernelGGL((tdc_kernel<MODE_UPDATE, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else if (mode == MODE_APPLY)
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else if (mode == MODE_RELERR)
     hipLaunchKernelGGL((tdc_kernel<MODE_RELERR, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else if (mode == MODE_COS)
     hipLaunchKernelGGL((tdc_kernel<MODE_COS, false>), g, t, 0, stream, in, b, prev, dst, n,
-                       partial, want, amax_out, gt);
+                       partial, want, amax_out, rt, gt);
   else
     hipLaunchKernelGGL((tdc_kernel<MODE_APPLY_AMAX, false>), g, t, 0, stream, in, b, prev, dst,
-                       n, partial, want, amax_out, gt);
+                       n, partial, want, amax_out, rt, gt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !want) return e;
   const int ncols = mode == MODE_UPDATE ? 4 : mode == MODE_COS ? 3 : 2;
-  hipLaunchKernelGGL(tdc_finalize_kernel, dim3(1), t, 0, stream, partial, (int)nb, ncols, sums, gt);
+  hipLaunchKernelGGL(tdc_finalize_kernel, dim3(1), t, 0, stream, partial, (int)nb, ncols, sums, rt,
+                     gt);
   return hipGetLastError();
 }
 

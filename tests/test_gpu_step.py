@@ -133,16 +133,46 @@ class _Stack:
             qa.act_quant(qa.INT8, xv, aq, self.a8[1], M=M, K=K, ldx=ldx)
             qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
 
-    def block(self, l, cur, out, fmts, gated):
+    def gemm(self, fmt, lay, y, gelu, K):
+        qa = self.qa
+        q, sc, ts, N, _ = lay
+        epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+        if fmt == 0:
+            aq = self.a4[0].view(-1)[: M * K // 2].view(M, K // 2)
+            asc = self.a4[1].view(-1)[: M * K // 16].view(M, K // 16)
+            qa.qlinear_nvfp4(aq, asc, self.a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
+        else:
+            aq = self.a8[0].view(-1)[: M * K].view(M, K)
+            qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
+
+    def routed_linear(self, flag, x, ldx, lay, y, gelu):
+        """One act_quant launch in the format the linear's flag selects, then
+        each format's GEMM under its gate."""
+        qa, t = self.qa, self.t
+        K = lay[4]
+        xv = t.as_strided(x, (M, K), (ldx, 1)).view(t.int16)
+        aq4 = self.a4[0].view(-1)[: M * K // 2].view(M, K // 2)
+        as4 = self.a4[1].view(-1)[: M * K // 16].view(M, K // 16)
+        aq8 = self.a8[0].view(-1)[: M * K].view(M, K)
+        qa.act_quant_routed(flag, xv, aq4, as4, self.a4[2], 0, self.qws, aq8, self.a8[1], M=M,
+                            K=K, ldx=ldx)
+        for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
+            with qa.gate(flag, bit):
+                self.gemm(fmt, lay, y, gelu, K)
+
+    def block(self, l, cur, out, fmts, gated, routed=False):
         """The compute path of block l (linears in formats fmts, or both
-        formats gated on the block's linear flags)."""
+        formats gated on the block's linear flags; routed: one act_quant
+        launch for both)."""
         qa, t = self.qa, self.t
         i16 = lambda b: b.view(t.int16)
         lay = self.layers[l]
         ins = [(cur, H, self.qkv, False), (self.qkv.view(-1)[2 * H:], 3 * H, self.o, False),
                (self.x1, H, self.u, True), (self.u, F, self.dd, False)]
         for j, (x, ldx, y, gelu) in enumerate(ins):
-            if gated:
+            if routed:
+                self.routed_linear(self.lin[l * J + j:], x, ldx, lay[j], y, gelu)
+            elif gated:
                 for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
                     with qa.gate(self.lin[l * J + j:], bit):
                         self.linear(fmt, x, ldx, lay[j], y, gelu)
@@ -198,8 +228,10 @@ class _Stack:
             rec.append((mask.copy(), skip.copy(), host(self.outs[-1]).copy()))
         return rec, tau
 
-    def device_step(self, tau, delta):
-        """One step, every path enqueued under its gate."""
+    def device_step(self, tau, delta, routed=False):
+        """One step, every path enqueued under its gate (routed: the calls
+        that take their format or ring slot from the gate byte, one launch
+        each)."""
         qa, t = self.qa, self.t
         i16 = lambda b: b.view(t.int16)
         qa.decide_step(self.sums, self.alpha_d, self.beta_d, tau, delta, L, J, self.t_ctr,
@@ -208,13 +240,22 @@ class _Stack:
         for l in range(L):
             out = self.outs[l]
             r0, r1 = self.ring[l]
-            for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
-                with qa.gate(self.blk[l:], bit):
-                    qa.tdc_apply(i16(cur), i16(slot), i16(out), self.sums[l, :2], self.rws)
-            self.block(l, cur, out, None, True)
-            for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
-                with qa.gate(self.blk[l:], bit):
-                    qa.tdc_update(i16(cur), i16(out), i16(prev), i16(nxt), self.sums[l], self.rws)
+            if routed:
+                qa.tdc_apply_ring(self.blk[l:], i16(cur), i16(r0), i16(r1), i16(out),
+                                  self.sums[l, :2], self.rws)
+            else:
+                for slot, bit in ((r0, qa.BLK_SKIP0), (r1, qa.BLK_SKIP1)):
+                    with qa.gate(self.blk[l:], bit):
+                        qa.tdc_apply(i16(cur), i16(slot), i16(out), self.sums[l, :2], self.rws)
+            self.block(l, cur, out, None, True, routed)
+            if routed:
+                qa.tdc_update_ring(self.blk[l:], i16(cur), i16(out), i16(r0), i16(r1),
+                                   self.sums[l], self.rws)
+            else:
+                for prev, nxt, bit in ((r0, r1, qa.BLK_RUN0), (r1, r0, qa.BLK_RUN1)):
+                    with qa.gate(self.blk[l:], bit):
+                        qa.tdc_update(i16(cur), i16(out), i16(prev), i16(nxt), self.sums[l],
+                                      self.rws)
             cur = out
 
 
@@ -227,8 +268,9 @@ def _inputs():
     return xs
 
 
+@pytest.mark.parametrize("routed", [False, True])
 @pytest.mark.parametrize("delta", [10.0, 0.05, 0.0])
-def test_device_decisions_eager_and_graph(delta):
+def test_device_decisions_eager_and_graph(delta, routed):
     # delta 10: every block that ran at t-1 is skipped from t = 2 on (both
     # paths, both ring slots); 0.05: the pages' threshold, some blocks;
     # 0: nothing is skipped
@@ -246,7 +288,7 @@ def test_device_decisions_eager_and_graph(delta):
     st.reset()
     for step, xd in enumerate(xs):
         st.x_in.copy_(xd)
-        st.device_step(tau, delta)
+        st.device_step(tau, delta, routed)
         t.cuda.synchronize()
         np.testing.assert_array_equal(host(st.mask_out), ref[step][0], err_msg=f"mask, step {step}")
         np.testing.assert_array_equal(host(st.skip_out), ref[step][1], err_msg=f"skip, step {step}")
@@ -259,7 +301,7 @@ def test_device_decisions_eager_and_graph(delta):
     s.wait_stream(t.cuda.current_stream())
     with t.cuda.stream(s):
         with t.cuda.graph(g, stream=s):
-            st.device_step(tau, delta)
+            st.device_step(tau, delta, routed)
     t.cuda.current_stream().wait_stream(s)
     st.reset()
     t.cuda.synchronize()
