@@ -139,8 +139,17 @@ def cpu_baseline(x, w, x_out, delta_prev, rows):
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
     flops = 2 * 2.0 * rows * N * K
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model,
             "sample": f"first {rows} of {M} token rows, one full step (both quantizers, both "
                       f"float64 GEMMs, TDC update/apply sums), {dt:.1f} s; element-wise numpy on "
                       f"1 thread, float64 BLAS on {cores} threads; host has {os.cpu_count()} CPUs"}
