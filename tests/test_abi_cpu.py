@@ -148,6 +148,31 @@ def test_convert_check_validation():
     assert _status("qa_test_convert", 0, 5, 0, FAKE, None) == 0              # nothing to do
 
 
+def test_routed_and_stage_validation():
+    # act_quant_routed: route byte and both formats' buffers required; shapes
+    # and alignment as act_quant; outputs must not overlap each other
+    A = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+    ok = [A[0], A[1], 64, 256, 256, A[2], A[3], A[4], 1, None, 0, A[5], A[6], None]
+    assert _status("act_quant_routed", None, *ok[1:]) == -1
+    bad_k = list(ok); bad_k[3] = 24; bad_k[4] = 24
+    assert _status("act_quant_routed", *bad_k) == -2
+    no_ws = list(ok); no_ws[8] = 0
+    assert _status("act_quant_routed", *no_ws) == -5
+    alias = list(ok); alias[11] = A[2]                              # q8 on q4
+    assert _status("act_quant_routed", *alias) == -7
+    # ring calls: the slots must not overlap each other or the other buffers
+    assert _status("tdc_update_ring", None, A[0], A[1], A[2], A[3], 64, A[4], A[5], 1 << 20,
+                   None) == -1
+    assert _status("tdc_update_ring", A[6], A[0], A[1], A[2], A[2], 64, A[4], A[5], 1 << 20,
+                   None) == -7
+    assert _status("tdc_apply_ring", A[6], A[0], A[2], A[3], A[2], 64, None, None, None, 0,
+                   None) == -7
+    # stage A/B: design and sizes checked before any launch
+    assert _status("qa_test_stage_ab", 3, 1, 1, A[0], A[1], None) == -1
+    assert _status("qa_test_stage_ab", 0, 1, 0, A[0], A[1], None) == -1
+    assert _status("qa_test_stage_ab", 0, 1, 1, ctypes.c_void_p(0x100002), A[1], None) == -3
+
+
 def test_strerror_covers_codes():
     for s in range(-8, 1):
         assert qa.strerror(s) != "unknown status"
