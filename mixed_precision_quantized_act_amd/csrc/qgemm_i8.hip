@@ -28,7 +28,8 @@
 // 128 columns).  K runs in units of 64 (two MFMA k-steps of 32): per unit
 // the tile's 16 KB of activations and 16 KB of plane rows are DMA'd
 // (buffer_load ... lds) into a 4-slot LDS ring, three units ahead; each wave
-// reads its fragments straight from the ring, one unit ahead.
+// reads its fragments straight from the ring, one unit ahead.  Both kinds of
+// memory instruction are spread over the unit's 32 MFMAs.
 #include <hip/hip_ext.h>
 
 #include "qgemm_common.h"
@@ -251,48 +252,52 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
                     (uint32_t)u_count * (uint32_t)kUnitBytes);
     constexpr uint32_t kOOB = 0x7FFFFFF0u;
 
-    // DMA of unit u into slot u % kSlots.  One instruction fills 1 KB of
-    // LDS: 16 activation rows (lane l: row l/4, LDS slot l%4 = chunk
-    // chunk_slot(row, l%4)), or 1 KB of the packed planes as they lie.
-    // Wave w moves the 1 KB blocks w, w+4, w+8, w+12 of each operand.
+    // DMA of unit u into slot u % kSlots, one instruction at a time (idx
+    // 0..7).  One instruction fills 1 KB of LDS: 16 activation rows (lane
+    // l: row l/4, LDS slot l%4 = chunk chunk_slot(row, l%4)), or 1 KB of
+    // the packed planes as they lie.  Wave w moves the 1 KB blocks w, w+4,
+    // w+8, w+12 of the activations (idx 0..3), then of the planes (4..7).
     // Units past the last are issued as zero loads into their free slot.
-    auto issue_unit = [&](int u) {
+    auto issue_one = [&](int u, int idx) {
       uint8_t* s = smem + (u % kSlots) * kSlot;
       const bool real = u < u_count;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int blk = wave + 4 * i;
+      const int blk = wave + 4 * (idx & 3);
+      if (idx < 4) {
         const uint32_t row = (uint32_t)(16 * blk + (lane >> 2));
         const uint32_t kb = (uint32_t)u * kUnitK + 16u * (uint32_t)chunk_slot((int)row, lane & 3);
         dma16(ra, s + blk * 1024, real && kb < a_lim ? row * (uint32_t)K + kb : kOOB);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int blk = wave + 4 * i;
+      } else {
         dma16(rw, s + kWOff + blk * 1024,
               real ? (uint32_t)u * kUnitBytes + (uint32_t)(blk * 1024 + lane * 16) : kOOB);
       }
     };
+    auto issue_unit = [&](int u) {
+#pragma unroll
+      for (int idx = 0; idx < kLoads; ++idx) issue_one(u, idx);
+    };
     // Fragments of a unit: for k-step s, lane (lh, lr) takes the 16 bytes
     // of K 32 s + 16 lh .. +15 of row 32 i + lr of the wave's activation
     // rows (tile i) and of plane row 32 j + lr (tile j).  Bit 2 of those
-    // rows is bit 2 of lr, so one swizzle serves all.
+    // rows is bit 2 of lr, so one swizzle serves all.  One read per idx
+    // (0..19): k-step idx / 10, activation tiles 0, 1, then plane tiles 0..7.
     struct Frag {
       i32x4 a[2][kFM];
       i32x4 w[2][kFN];
     };
-    auto read_unit = [&](int u, Frag& f) {
+    constexpr int kReads = 2 * (kFM + kFN);
+    auto read_one = [&](int u, int idx, Frag& f) {
       const uint8_t* s = smem + (u % kSlots) * kSlot;
+      const int ks = idx / (kFM + kFN), r = idx % (kFM + kFN);
+      const int off = 16 * chunk_slot(lr, 2 * ks + lh);
+      if (r < kFM)
+        f.a[ks][r] = *reinterpret_cast<const i32x4*>(s + (64 * wave + 32 * r + lr) * 64 + off);
+      else
+        f.w[ks][r - kFM] =
+            *reinterpret_cast<const i32x4*>(s + kWOff + (32 * (r - kFM) + lr) * 64 + off);
+    };
+    auto read_unit = [&](int u, Frag& f) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int off = 16 * chunk_slot(lr, 2 * ks + lh);
-#pragma unroll
-        for (int i = 0; i < kFM; ++i)
-          f.a[ks][i] = *reinterpret_cast<const i32x4*>(s + (64 * wave + 32 * i + lr) * 64 + off);
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-          f.w[ks][j] = *reinterpret_cast<const i32x4*>(s + kWOff + (32 * j + lr) * 64 + off);
-      }
+      for (int idx = 0; idx < kReads; ++idx) read_one(u, idx, f);
     };
     auto pin_frag = [](Frag& f) {
 #pragma unroll
@@ -311,34 +316,43 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
     auto wait_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
     // MFMA issued as W x A^T: accumulator r of tile (i, j) is output row
     // 32 i + lr of the wave's rows and plane row 32 j + 8 (r/4) + 4 lh + r%4.
-    // The next unit's 20 fragment reads are interleaved with the 32 MFMAs.
-    auto compute = [&](Frag& cur, int u_next, Frag& nxt) {
+    // The 32 MFMAs of a unit run in 8 segments of 4; segment g also issues
+    // DMA instruction g of unit u_dma and reads kFirst[g] .. kFirst[g+1]-1
+    // of unit u_next, so that the memory instructions trickle out under
+    // the MFMAs (a burst of 8 LDS-DMA instructions after the barrier holds
+    // the wave's issue long enough to idle its MFMA unit: measured 7-9 %
+    // slower at the CogVideoX linear shapes).
+    auto compute = [&](Frag& cur, int u_next, Frag& nxt, int u_dma) {
+      constexpr int kSegs = 8;
+      static_assert(kLoads == kSegs && 2 * kFM * kFN == 4 * kSegs, "segment layout");
+      constexpr int kFirst[kSegs + 1] = {0, 3, 6, 9, 12, 14, 16, 18, kReads};
       pin_frag(cur);
-      read_unit(u_next, nxt);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int seg = 0; seg < kSegs; ++seg) {
 #pragma unroll
-        for (int i = 0; i < kFM; ++i)
+        for (int m = 0; m < 4; ++m) {
+          const int x = seg * 4 + m, ks = x / (kFM * kFN), i = (x / kFN) % kFM, j = x % kFN;
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.w[ks][j], cur.a[ks][i],
+                                                            acc[i][j], 0, 0, 0);
+        }
+        issue_one(u_dma, seg);
 #pragma unroll
-          for (int j = 0; j < kFN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.w[ks][j], cur.a[ks][i],
-                                                              acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int x = 0; x < 2 * kFM * kFN; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-        if (x < 2 * (kFM + kFN)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        for (int r = 0; r < 3; ++r)
+          if (kFirst[seg] + r < kFirst[seg + 1]) read_one(u_next, kFirst[seg] + r, nxt);
+        __builtin_amdgcn_sched_barrier(0);
       }
       pin_frag(nxt);
     };
     // Unit u: wait for this wave's DMA of unit u+1 (units u+2, u+3 may still
     // be in flight) and for its reads of unit u (done one unit earlier);
     // after the barrier unit u+1 is visible to every wave and no wave reads
-    // the slot of unit u any more, so it takes unit u + kSlots.
-    auto sync_unit = [&](int u) {
+    // the slot of unit u any more, so that compute(u) may DMA unit u +
+    // kSlots into it.
+    auto sync_unit = [&] {
+      __builtin_amdgcn_sched_barrier(0);
       wait_vm<(kSlots - 2) * kLoads>();
       wait_lds();
       barrier();
-      issue_unit(u + kSlots);
     };
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) issue_unit(u);
@@ -348,10 +362,10 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
     read_unit(0, f0);
     if constexpr (kFactors) put_factors();
     for (int u = 0; u < u_count; u += 2) {
-      sync_unit(u);
-      compute(f0, u + 1, f1);
-      sync_unit(u + 1);
-      compute(f1, u + 2, f0);
+      sync_unit();
+      compute(f0, u + 1, f1, u + kSlots);
+      sync_unit();
+      compute(f1, u + 2, f0, u + 1 + kSlots);
     }
     wait_vm<0>();       // no DMA into LDS outlives the workgroup
     wait_lds();
