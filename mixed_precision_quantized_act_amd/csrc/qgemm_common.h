@@ -105,16 +105,18 @@ __host__ __device__ constexpr bool epi_staged(int k) {
 // ------------------------------------------------------------- epilogue --
 
 // Output of one wave's (32 FM) x 128 block: the wave's rows start at
-// wave_row0, its columns at wave_col0.  acc[i][j] holds the float32 sums
-// as an MFMA issued W x A^T leaves them: lane (h, c) = (lane / 32, lane %
-// 32) of tile (i, j) owns row 32 i + c and, for q = 0..3, the 4 consecutive
-// columns 32 j + 8 q + 4 h .. +3 (registers 4 q .. 4 q + 3).  Every output
+// wave_row0, its columns at wave_col0.  acc(i, j, r) gives the float32 sum
+// in register r of MFMA tile (i, j) as an MFMA issued W x A^T leaves it:
+// lane (h, c) = (lane / 32, lane % 32) of tile (i, j) owns row 32 i + c
+// and, for q = 0..3, the 4 consecutive columns 32 j + 8 q + 4 h .. +3
+// (registers 4 q .. 4 q + 3); it is called where the value is consumed, so
+// that values derived from the accumulators need not all be live.  Every output
 // is acc * rs[i] (the row's scale), then + bias, then GELU, then rounded to
 // the output type; rows and columns past the output read the last valid
 // bias entry and are never stored.  stg: this wave's 8 KB (per pass of 32
 // rows) of idle LDS for the staged bf16 kinds.
-template <int kEpi, int FM>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const float (&rs)[FM],
+template <int kEpi, int FM, class Acc>
+__device__ __forceinline__ void store_tile(const Acc& acc, const float (&rs)[FM],
                                            int64_t wave_row0, int64_t wave_col0, uint8_t* stg,
                                            const EpiArgs& e, int lane) {
   const int c = lane & 31, lh = lane >> 5;
@@ -146,11 +148,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const flo
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x16& a = acc[i][j];
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              v[t] = a[4 * q + t] * rs[i];
+              v[t] = acc(i, j, 4 * q + t) * rs[i];
               if constexpr (kBias) v[t] += bv[j][q][t];
               if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
             }
@@ -174,6 +175,24 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const flo
         const int r = it * 4 + (lane >> 4);
         d[it] = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((k ^ (r & 15)) << 4));
       }
+      if (cols_left >= 128 && e.ldy < (1 << 24)) {
+        // whole 256-byte row segments: buffer stores over this pass's rows
+        // that exist; rows past the output fall outside the buffer's range
+        // and are dropped (the whole offset is in the vector offset, which
+        // the range check covers; the scalar offset stays 0)
+        const uint32_t row_bytes = 2u * (uint32_t)e.ldy;
+        const uint32_t nrows = (uint32_t)max<int64_t>(0, min<int64_t>(rows_left, 32 * kPassTiles));
+        const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(ybase, nrows * row_bytes);
+        const uint32_t voff = (uint32_t)(lane >> 4) * row_bytes + (uint32_t)k * 16u;
+#pragma unroll
+        for (int it = 0; it < 8 * kPassTiles; ++it) {
+          __builtin_amdgcn_raw_buffer_store_b128(d[it], ry, (int)(voff + (uint32_t)it * 4u * row_bytes),
+                                                 0, 0);
+          if constexpr (epi_amax(kEpi))
+            if (it * 4 + (lane >> 4) < rows_left)
+              amx = max(amx, fold_max(abs_max8_pk(d[it], u16x2{0, 0})));
+        }
+      } else {
 #pragma unroll
       for (int it = 0; it < 8 * kPassTiles; ++it) {
         const int r = it * 4 + (lane >> 4);
@@ -190,6 +209,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const flo
             }
           }
         }
+      }
       }
       // the next pass overwrites the slice after these reads (in order)
       asm volatile("" ::: "memory");
@@ -234,7 +254,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const flo
             float v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-              v[t] = acc[i][j][4 * (2 * p + (t >> 2)) + (t & 3)] * rs[i];
+              v[t] = acc(i, j, 4 * (2 * p + (t >> 2)) + (t & 3)) * rs[i];
               if constexpr (kBias) v[t] += bv[t];
               if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
             }
@@ -288,7 +308,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][4], const flo
             float v[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              v[t] = acc[i][j][4 * q + t] * rs[i];
+              v[t] = acc(i, j, 4 * q + t) * rs[i];
               if constexpr (kBias) v[t] += bv[t];
               if constexpr (kGelu) v[t] = gelu_tanh(v[t]);
             }

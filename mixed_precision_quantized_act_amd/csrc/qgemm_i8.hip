@@ -451,19 +451,13 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           cf[j][q] = *reinterpret_cast<const f32x4*>(colf + 32 * j + 8 * q + 4 * lh);
-      f32x16 accf[kFM][kFN / 2];
-#pragma unroll
-      for (int j = 0; j < kFN / 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < kFM; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              accf[i][j][4 * q + t] = __builtin_fmaf((float)acc[i][j + kFN / 2][4 * q + t], 256.0f,
-                                                     (float)acc[i][j][4 * q + t]) *
-                                      cf[j][q][t];
-      store_tile<kEpi, kFM>(accf, rs, wave_row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
+      // formed where the epilogue consumes it, so that only the values of
+      // the pass being stored are live in ordinary registers
+      auto val = [&](int i, int j, int r) {
+        return __builtin_fmaf((float)acc[i][j + kFN / 2][r], 256.0f, (float)acc[i][j][r]) *
+               cf[j][r >> 2][r & 3];
+      };
+      store_tile<kEpi, kFM>(val, rs, wave_row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
     }
   }
 }
