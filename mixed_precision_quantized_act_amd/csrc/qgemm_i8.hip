@@ -185,6 +185,148 @@ struct I8Args {
 // the test-only epilogue: store H and L themselves
 constexpr int kEpiAcc = 100;
 
+// ---- pieces of the pipeline shared by the two GEMM kernels
+namespace {
+
+constexpr uint32_t kOOB = 0x7FFFFFF0u;          // an offset past every buffer range
+
+// MFMA operands of one unit for a wave: for k-step s, lane (lh, lr) holds
+// the 16 bytes of K 32 s + 16 lh .. +15 of row 32 i + lr of the wave's
+// activation rows (tile i) and of plane row 32 j + lr (tile j).
+struct Frag {
+  i32x4 a[2][kFM];
+  i32x4 w[2][kFN];
+};
+constexpr int kReads = 2 * (kFM + kFN);          // fragment reads per unit
+
+// DMA instruction idx (0..7) of unit u into the ring slot at s.  One
+// instruction fills 1 KB of LDS: 16 activation rows (lane l: row l/4, LDS
+// chunk l%4 = chunk chunk_slot(row, l%4)), or 1 KB of the packed planes as
+// they lie.  Wave w moves the 1 KB blocks w, w+4, w+8, w+12 of the
+// activations (idx 0..3), then of the planes (4..7).  ra: the tile's
+// activation rows from the unit base (a_lim bytes of K left in a row);
+// rw: its planes from the same unit.  real = false: zero loads.
+__device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rw,
+                                        uint8_t* s, uint32_t u, int idx, int wave, int ln,
+                                        uint32_t K, uint32_t a_lim, bool real) {
+  const int blk = wave + 4 * (idx & 3);
+  if (idx < 4) {
+    const uint32_t row = (uint32_t)(16 * blk + (ln >> 2));
+    const uint32_t kb = u * kUnitK + 16u * (uint32_t)chunk_slot((int)row, ln & 3);
+    dma16(ra, s + blk * 1024, real && kb < a_lim ? row * K + kb : kOOB);
+  } else {
+    dma16(rw, s + kWOff + blk * 1024,
+          real ? u * kUnitBytes + (uint32_t)(blk * 1024 + ln * 16) : kOOB);
+  }
+}
+
+// Fragment read idx (0..19: k-step idx / 10; activation tiles 0, 1, then
+// plane tiles 0..7) of the unit in the ring slot at s.  Bit 2 of the rows
+// read is bit 2 of lr, so one swizzle serves all.
+__device__ __forceinline__ void read_one(const uint8_t* s, int idx, Frag& f, int wave, int ln) {
+  const int ks = idx / (kFM + kFN), r = idx % (kFM + kFN);
+  const int lr = ln & 31;
+  const int off = 16 * chunk_slot(lr, 2 * ks + (ln >> 5));
+  if (r < kFM)
+    f.a[ks][r] = *reinterpret_cast<const i32x4*>(s + (64 * wave + 32 * r + lr) * 64 + off);
+  else
+    f.w[ks][r - kFM] =
+        *reinterpret_cast<const i32x4*>(s + kWOff + (32 * (r - kFM) + lr) * 64 + off);
+}
+
+// fragments are in their registers at this point of the program
+__device__ __forceinline__ void pin_frag(Frag& f) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) asm volatile("" : "+v"(f.a[ks][i]));
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) asm volatile("" : "+v"(f.w[ks][j]));
+  }
+}
+
+// a workgroup barrier that the compiler moves no instruction across
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// the lane index as an opaque value: offsets formed from it are formed
+// where it is taken rather than hoisted and kept live
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
+// The 32 MFMAs of a unit on cur, issued as W x A^T (accumulator r of tile
+// (i, j): output row 32 i + lr of the wave's rows, plane row 32 j + 8 (r/4)
+// + 4 lh + r%4), in 8 segments of 4.  With kMem, segment g also issues DMA
+// instruction g (dma(g)) and the fragment reads kFirstRead[g] ..
+// kFirstRead[g+1]-1 (read(idx)), so that the memory instructions trickle
+// out under the MFMAs (a burst of 8 LDS-DMA instructions after the barrier
+// holds the wave's issue long enough to idle its MFMA unit: measured 7-9 %
+// slower at the CogVideoX linear shapes).  kFirst: the first k-step starts
+// the sums from zero.
+template <bool kFirst, bool kMem, class Dma, class Read>
+__device__ __forceinline__ void unit_mfmas(i32x16 (&acc)[kFM][kFN], Frag& cur, const Dma& dma,
+                                           const Read& read) {
+  constexpr int kSegs = 8;
+  static_assert(kLoads == kSegs && 2 * kFM * kFN == 4 * kSegs, "segment layout");
+  constexpr int kFirstRead[kSegs + 1] = {0, 3, 6, 9, 12, 14, 16, 18, kReads};
+  const i32x16 zero = {};
+  pin_frag(cur);
+#pragma unroll
+  for (int seg = 0; seg < kSegs; ++seg) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int x = seg * 4 + m, ks = x / (kFM * kFN), i = (x / kFN) % kFM, j = x % kFN;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.w[ks][j], cur.a[ks][i],
+                                                        kFirst && ks == 0 ? zero : acc[i][j],
+                                                        0, 0, 0);
+    }
+    if constexpr (kMem) {
+      dma(seg);
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        if (kFirstRead[seg] + r < kFirstRead[seg + 1]) read(kFirstRead[seg] + r);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Epilogue of a wave's 64 rows x 128 columns: 256 H + L in float32 (one
+// rounding: fmaf of two exact conversions while |H|, |L| < 2^24), times
+// 2^(X[n] - 1) of the column (colf, LDS), times the row scale rows[r] *
+// rs_mul (LDS), then store_tile with its staging at stg.  ln: the lane;
+// lr, lh: ln % 32 and ln / 32.
+template <int kEpi>
+__device__ __forceinline__ void i8_epilogue(const i32x16 (&acc)[kFM][kFN], const float* colf,
+                                            const float* rows, float rs_mul, int64_t wave_row0,
+                                            int64_t n0, uint8_t* stg, const EpiArgs& e, int wave,
+                                            int ln, int lr, int lh) {
+  float rs[kFM];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i) rs[i] = rows[64 * wave + 32 * i + lr] * rs_mul;
+  f32x4 cf[kFN / 2][4];
+#pragma unroll
+  for (int j = 0; j < kFN / 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      cf[j][q] = *reinterpret_cast<const f32x4*>(colf + 32 * j + 8 * q + 4 * lh);
+  // formed where the epilogue consumes it, so that only the values of the
+  // pass being stored are live in ordinary registers
+  auto val = [&](int i, int j, int r) {
+    return __builtin_fmaf((float)acc[i][j + kFN / 2][r], 256.0f, (float)acc[i][j][r]) *
+           cf[j][r >> 2][r & 3];
+  };
+  store_tile<kEpi, kFM>(val, rs, wave_row0, n0, stg, e, ln);
+}
+
+}  // namespace
+
+
 template <int kEpi, int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 qgemm_i8_kernel(I8Args g, EpiArgs e) {
@@ -250,97 +392,25 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
     const __amdgpu_buffer_rsrc_t rw =
         buffer_rsrc(g.planes + ((int64_t)tn * g.units + u_begin) * kUnitBytes,
                     (uint32_t)u_count * (uint32_t)kUnitBytes);
-    constexpr uint32_t kOOB = 0x7FFFFFF0u;
-
-    // DMA of unit u into slot u % kSlots, one instruction at a time (idx
-    // 0..7).  One instruction fills 1 KB of LDS: 16 activation rows (lane
-    // l: row l/4, LDS slot l%4 = chunk chunk_slot(row, l%4)), or 1 KB of
-    // the packed planes as they lie.  Wave w moves the 1 KB blocks w, w+4,
-    // w+8, w+12 of the activations (idx 0..3), then of the planes (4..7).
-    // Units past the last are issued as zero loads into their free slot.
+    // DMA of unit u into slot u % kSlots; units past the last are issued
+    // as zero loads into their free slot
     auto issue_one = [&](int u, int idx) {
-      uint8_t* s = smem + (u % kSlots) * kSlot;
-      const bool real = u < u_count;
-      const int blk = wave + 4 * (idx & 3);
-      if (idx < 4) {
-        const uint32_t row = (uint32_t)(16 * blk + (lane >> 2));
-        const uint32_t kb = (uint32_t)u * kUnitK + 16u * (uint32_t)chunk_slot((int)row, lane & 3);
-        dma16(ra, s + blk * 1024, real && kb < a_lim ? row * (uint32_t)K + kb : kOOB);
-      } else {
-        dma16(rw, s + kWOff + blk * 1024,
-              real ? (uint32_t)u * kUnitBytes + (uint32_t)(blk * 1024 + lane * 16) : kOOB);
-      }
+      dma_one(ra, rw, smem + (u % kSlots) * kSlot, (uint32_t)u, idx, wave, lane, (uint32_t)K,
+              a_lim, u < u_count);
     };
     auto issue_unit = [&](int u) {
 #pragma unroll
       for (int idx = 0; idx < kLoads; ++idx) issue_one(u, idx);
     };
-    // Fragments of a unit: for k-step s, lane (lh, lr) takes the 16 bytes
-    // of K 32 s + 16 lh .. +15 of row 32 i + lr of the wave's activation
-    // rows (tile i) and of plane row 32 j + lr (tile j).  Bit 2 of those
-    // rows is bit 2 of lr, so one swizzle serves all.  One read per idx
-    // (0..19): k-step idx / 10, activation tiles 0, 1, then plane tiles 0..7.
-    struct Frag {
-      i32x4 a[2][kFM];
-      i32x4 w[2][kFN];
-    };
-    constexpr int kReads = 2 * (kFM + kFN);
-    auto read_one = [&](int u, int idx, Frag& f) {
-      const uint8_t* s = smem + (u % kSlots) * kSlot;
-      const int ks = idx / (kFM + kFN), r = idx % (kFM + kFN);
-      const int off = 16 * chunk_slot(lr, 2 * ks + lh);
-      if (r < kFM)
-        f.a[ks][r] = *reinterpret_cast<const i32x4*>(s + (64 * wave + 32 * r + lr) * 64 + off);
-      else
-        f.w[ks][r - kFM] =
-            *reinterpret_cast<const i32x4*>(s + kWOff + (32 * (r - kFM) + lr) * 64 + off);
-    };
     auto read_unit = [&](int u, Frag& f) {
 #pragma unroll
-      for (int idx = 0; idx < kReads; ++idx) read_one(u, idx, f);
+      for (int idx = 0; idx < kReads; ++idx) read_one(smem + (u % kSlots) * kSlot, idx, f, wave, lane);
     };
-    auto pin_frag = [](Frag& f) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int i = 0; i < kFM; ++i) asm volatile("" : "+v"(f.a[ks][i]));
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) asm volatile("" : "+v"(f.w[ks][j]));
-      }
-    };
-    auto barrier = [] {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_barrier" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto wait_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-    // MFMA issued as W x A^T: accumulator r of tile (i, j) is output row
-    // 32 i + lr of the wave's rows and plane row 32 j + 8 (r/4) + 4 lh + r%4.
-    // The 32 MFMAs of a unit run in 8 segments of 4; segment g also issues
-    // DMA instruction g of unit u_dma and reads kFirst[g] .. kFirst[g+1]-1
-    // of unit u_next, so that the memory instructions trickle out under
-    // the MFMAs (a burst of 8 LDS-DMA instructions after the barrier holds
-    // the wave's issue long enough to idle its MFMA unit: measured 7-9 %
-    // slower at the CogVideoX linear shapes).
+    // unit u on cur, with the DMA of unit u_dma and the reads of unit u_next
     auto compute = [&](Frag& cur, int u_next, Frag& nxt, int u_dma) {
-      constexpr int kSegs = 8;
-      static_assert(kLoads == kSegs && 2 * kFM * kFN == 4 * kSegs, "segment layout");
-      constexpr int kFirst[kSegs + 1] = {0, 3, 6, 9, 12, 14, 16, 18, kReads};
-      pin_frag(cur);
-#pragma unroll
-      for (int seg = 0; seg < kSegs; ++seg) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int x = seg * 4 + m, ks = x / (kFM * kFN), i = (x / kFN) % kFM, j = x % kFN;
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.w[ks][j], cur.a[ks][i],
-                                                            acc[i][j], 0, 0, 0);
-        }
-        issue_one(u_dma, seg);
-#pragma unroll
-        for (int r = 0; r < 3; ++r)
-          if (kFirst[seg] + r < kFirst[seg + 1]) read_one(u_next, kFirst[seg] + r, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      unit_mfmas<false, true>(
+          acc, cur, [&](int idx) { issue_one(u_dma, idx); },
+          [&](int idx) { read_one(smem + (u_next % kSlots) * kSlot, idx, nxt, wave, lane); });
       pin_frag(nxt);
     };
     // Unit u: wait for this wave's DMA of unit u+1 (units u+2, u+3 may still
@@ -352,12 +422,12 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<(kSlots - 2) * kLoads>();
       wait_lds();
-      barrier();
+      ring_barrier();
     };
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) issue_unit(u);
     wait_vm<(kSlots - 1) * kLoads>();
-    barrier();
+    ring_barrier();
     Frag f0, f1;
     read_unit(0, f0);
     if constexpr (kFactors) put_factors();
@@ -439,9 +509,9 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
           }
       }
     } else {
-      // 256 H + L in float32 (one rounding: fmaf of two exact conversions
-      // while |H|, |L| < 2^24), times 2^(X[n] - 1) of the column; the row
-      // scale s_a s_Tw is the epilogue's rs.
+      // rows holds s_a s_Tw (multiplied once per row as it was staged)
+      // i8_epilogue's arithmetic, written out: called here, the register
+      // allocation of this kernel spills 12-37 registers
       float rs[kFM];
 #pragma unroll
       for (int i = 0; i < kFM; ++i) rs[i] = rows[64 * wave + 32 * i + lr];
@@ -451,8 +521,6 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           cf[j][q] = *reinterpret_cast<const f32x4*>(colf + 32 * j + 8 * q + 4 * lh);
-      // formed where the epilogue consumes it, so that only the values of
-      // the pass being stored are live in ordinary registers
       auto val = [&](int i, int j, int r) {
         return __builtin_fmaf((float)acc[i][j + kFN / 2][r], 256.0f, (float)acc[i][j][r]) *
                cf[j][r >> 2][r & 3];
@@ -460,6 +528,166 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
       store_tile<kEpi, kFM>(val, rs, wave_row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
     }
   }
+}
+
+// Persistent whole-tile kernel for short K loops: a grid of one workgroup
+// per CU, each taking the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
+// the whole-tile order (gridDim.x a multiple of 8, so that a workgroup
+// stays in its XCD's range).  The units of a workgroup's tiles form one
+// stream through the LDS ring: the DMA of the next tile's first three units
+// runs under the current tile's last units, so that a tile starts without
+// a fresh workgroup's launch and first-load latency.  At a tile's end:
+//   - the last unit issues no DMA and no reads, so that its slot is free
+//     for the epilogue's staging;
+//   - before the epilogue, every DMA issued so far has landed (the next
+//     tile's units 0 .. 2): the epilogue's stores are then the only
+//     memory operations in flight older than later DMAs, and no
+//     count-based wait assumes an order between loads and stores (a
+//     tile's first two syncs wait for no DMA);
+//   - after it, wave 0 DMAs the next tile's factors, every wave the next
+//     tile's unit 3 (into the staging slot), then reads unit 0.
+// Requires an even number of units, at least 6.
+template <int kEpi>
+__global__ void __launch_bounds__(kThreads, 1)
+qgemm_i8_persist(I8Args g, EpiArgs e) {
+  // the ring, then the tile's 128 column factors and 256 activation row
+  // scales s_a, both moved in by DMA (1 KB each)
+  constexpr int kPColF = kSlots * kSlot, kPRowS = kPColF + 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPRowS + 1024];
+  static_assert(kPRowS + 1024 <= 160 * 1024, "LDS");
+  static_assert(kSlot >= 4 * 8192 * kPassTiles, "epilogue staging in one ring slot");
+  static_assert((kSlots & (kSlots - 1)) == 0, "ring of a power of two");
+  if (gated_off(g.gate)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int units = g.units;
+  const uint32_t K = (uint32_t)g.K;
+
+  // tile k of this workgroup: origin and operand ranges (rows past M fall
+  // outside the activation range and load zero); past the last tile ok =
+  // false and the ranges are empty, so that its loads are all zero
+  struct Tile {
+    int64_t m0, n0;
+    const uint8_t* a;
+    const int8_t* w;
+    uint32_t a_bytes, w_bytes;
+    bool ok;
+  };
+  auto tile_k = [&](int k, Tile& t) {
+    const int bid = (int)blockIdx.x + k * (int)gridDim.x;
+    TileWork tw;
+    t.ok = bid < g.grid_main &&
+           tile_work(kWhole, bid, g.main_tiles, g.splits, g.split_units, units, tw);
+    int tm = 0, tn = 0;
+    if (t.ok) tile_coords(tw.logical, g.mt, g.nt, 8, tm, tn);
+    t.m0 = (int64_t)tm * kTileM;
+    t.n0 = (int64_t)tn * kTileN;
+    t.a = g.a + t.m0 * g.K;
+    t.w = g.planes + (int64_t)tn * units * kUnitBytes;
+    t.a_bytes = t.ok ? (uint32_t)(min<int64_t>(e.M - t.m0, kTileM) * g.K) : 0u;
+    t.w_bytes = t.ok ? (uint32_t)units * (uint32_t)kUnitBytes : 0u;
+  };
+  Tile cur, nxt;
+  tile_k(0, cur);
+  if (!cur.ok) return;
+
+  // ring slot of unit u of the current tile (u >= units: the next tile's
+  // unit u - units), stream position sbase + u
+  int sbase = 0;
+  auto slot = [&](int u) { return smem + ((sbase + u) & (kSlots - 1)) * kSlot; };
+  // the DMA of unit u of the stream, instruction idx
+  auto issue_one = [&](int u, int idx, int ln) {
+    const bool in_next = u >= units;
+    const Tile& t = in_next ? nxt : cur;
+    dma_one(buffer_rsrc(t.a, t.a_bytes), buffer_rsrc(t.w, t.w_bytes), slot(u),
+            (uint32_t)(in_next ? u - units : u), idx, wave, ln, K, K, true);
+  };
+  // the factors of tile t by wave 0, 4 bytes per lane: 2^(X[n] - 1) of its
+  // 128 columns (the array is padded to whole tiles) and s_a of its 256
+  // rows (rows past M fall outside the range and read 0; never stored)
+  const float* const colf = reinterpret_cast<const float*>(smem + kPColF);
+  const float* const rows = reinterpret_cast<const float*>(smem + kPRowS);
+  auto dma_factors = [&](const Tile& t) {
+    if (wave != 0) return;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(g.rowf + t.n0, kTileN * 4);
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(
+        g.a_rs + t.m0, (uint32_t)(min<int64_t>(e.M - t.m0, kTileM) * 4));
+#pragma unroll
+    for (int i = 0; i < kTileN / 64; ++i) dma4(rc, smem + kPColF + 256 * i, 256u * i + 4u * lane);
+#pragma unroll
+    for (int i = 0; i < kTileM / 64; ++i) dma4(rr, smem + kPRowS + 256 * i, 256u * i + 4u * lane);
+  };
+  // before unit u (u >= 2): this wave's DMA of unit u+1 has landed (units
+  // u+2, u+3 may be in flight); before units 0 and 1 nothing is in flight
+  // that they need.  Then this wave's reads are done, then the barrier.
+  auto sync_unit = [&](auto vm) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(vm)::value) wait_vm<(kSlots - 2) * kLoads>();
+    wait_lds();
+    ring_barrier();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  i32x16 acc[kFM][kFN];
+  // unit u on cur: with the DMA of unit u + kSlots and the reads of unit
+  // u + 1 into nf (kMem), the first unit starting the sums (first)
+  auto compute = [&](auto first, auto mem, Frag& cf_, int u, Frag& nf, int ln) {
+    unit_mfmas<decltype(first)::value, decltype(mem)::value>(
+        acc, cf_, [&](int idx) { issue_one(u + kSlots, idx, ln); },
+        [&](int idx) { read_one(slot(u + 1), idx, nf, wave, ln); });
+    if constexpr (decltype(mem)::value) pin_frag(nf);
+  };
+
+  // first tile: its factors, then units 0 .. kSlots - 1, all landed
+  dma_factors(cur);
+  tile_k(1, nxt);
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+    for (int idx = 0; idx < kLoads; ++idx) issue_one(u, idx, lane);
+  wait_vm<0>();
+  ring_barrier();
+  Frag f0, f1;
+#pragma unroll
+  for (int idx = 0; idx < kReads; ++idx) read_one(slot(0), idx, f0, wave, lane);
+
+  for (int k = 0;; ++k) {
+    // per-lane offsets formed once per tile (live through its unit loop,
+    // not through the epilogue)
+    const int ln = opaque_lane(lane);
+    sync_unit(F());
+    compute(T(), T(), f0, 0, f1, ln);
+    sync_unit(F());
+    compute(F(), T(), f1, 1, f0, ln);
+    for (int u = 2; u < units - 2; u += 2) {
+      sync_unit(T());
+      compute(F(), T(), f0, u, f1, ln);
+      sync_unit(T());
+      compute(F(), T(), f1, u + 1, f0, ln);
+    }
+    sync_unit(T());
+    compute(F(), T(), f0, units - 2, f1, ln);
+    sync_unit(T());
+    compute(F(), F(), f1, units - 1, f0, ln);
+    wait_vm<0>();
+    const int lne = opaque_lane(lane);
+    i8_epilogue<kEpi>(acc, colf, rows, *g.w_ts, cur.m0 + 64 * wave, cur.n0,
+                      slot(units - 1) + wave * 8192 * kPassTiles, e, wave, lne, lne & 31, lne >> 5);
+    // every wave is past its reads of the staging slot and of the factors
+    wait_lds();
+    ring_barrier();
+    if (!nxt.ok) break;
+    dma_factors(nxt);
+    const int ln2 = opaque_lane(lane);
+#pragma unroll
+    for (int idx = 0; idx < kLoads; ++idx) issue_one(units + kSlots - 1, idx, ln2);
+#pragma unroll
+    for (int idx = 0; idx < kReads; ++idx) read_one(slot(units), idx, f0, wave, ln2);
+    cur = nxt;
+    sbase = (sbase + units) & (kSlots - 1);
+    tile_k(k + 2, nxt);
+  }
+  wait_vm<0>();   // no DMA into LDS outlives the workgroup
 }
 
 // ------------------------------------------------------------------ host --
@@ -483,11 +711,31 @@ void launch_mode(int grid, hipEvent_t before, hipEvent_t after, const I8Args& g,
     hipLaunchKernelGGL((qgemm_i8_kernel<kEpi, kMode>), dim3(grid), dim3(kThreads), 0, st, g, e);
 }
 
+// the persistent kernel where a tile's start and end weigh most: short K
+// loops (even, 6 .. kPersistMaxUnits units) over more than one round of
+// tiles (measured 5-6 % faster at K = 1920, 1.6 % at 3072, 1 % slower at
+// 7680, where the static assignment of tiles to workgroups costs more)
+constexpr int kPersistMaxUnits = 64;
+
 template <int kEpi>
 void launch_one(const I8Args& g, const EpiArgs& e, hipStream_t st) {
   const int tail = g.mt * g.nt - g.main_tiles;
-  if (g.main_tiles)
+  bool persist = false;
+  if constexpr (kEpi != kEpiAcc)
+    persist = g.units % 2 == 0 && g.units >= 6 && g.units <= kPersistMaxUnits &&
+              g.grid_main > kCUs;
+  if (g.main_tiles && persist) {
+    if constexpr (kEpi != kEpiAcc) {
+      hipEvent_t after = tail ? nullptr : g_ev_after;
+      if (g_ev_before || after)
+        hipExtLaunchKernelGGL((qgemm_i8_persist<kEpi>), dim3(kCUs), dim3(kThreads), 0, st,
+                              g_ev_before, after, 0u, g, e);
+      else
+        hipLaunchKernelGGL((qgemm_i8_persist<kEpi>), dim3(kCUs), dim3(kThreads), 0, st, g, e);
+    }
+  } else if (g.main_tiles) {
     launch_mode<kEpi, kWhole>(g.grid_main, g_ev_before, tail ? nullptr : g_ev_after, g, e, st);
+  }
   if (!tail) return;
   launch_mode<kEpiPlain, kSlice>(tail * g.splits, g.main_tiles ? nullptr : g_ev_before, nullptr,
                                  g, e, st);

@@ -273,6 +273,60 @@ def test_quantized_output_and_amax(M, N, K):
     np.testing.assert_array_equal(host(ys), osc)
 
 
+# shapes that run the persistent whole-tile kernel (more than 256 whole
+# tiles, an even number of 6 .. 64 units), all with ragged M: 288 tiles (32
+# workgroups take a second tile) with ragged N at 30 and 6 units; 432 tiles
+# at 64 units; 540 tiles whose last round is split along K (512 whole
+# tiles, two per workgroup, then the slices and their fixup)
+PERSIST_SHAPES = [(4452, 1960, 1920), (4452, 1960, 384), (4452, 2984, 4096), (4452, 3840, 3840)]
+
+
+@pytest.mark.parametrize("M,N,K", PERSIST_SHAPES)
+def test_persistent_tiles(M, N, K):
+    qa, t = _qa(), torch()
+    x, w = _case(M, N, K, seed=51)
+    a = Q.int8_encode(x)
+    wq = Q.nvfp4_encode(w)
+    w8 = planes(wq, N, K)
+    rows = sample_rows(M, 24, seed=52)
+    # float32 outputs element by element on sampled rows (every tile row's
+    # first rows, the ragged last tile row, all columns)
+    rows = np.union1d(rows, np.arange(0, M, 256))
+    H, L, X = _oracle_sums(a[0], wq, rows)
+    Y = G.int8_linear_from_sums(H, L, X, a[1][rows], wq[2])
+    y = _out(run_i8(a, wq, w8, M, N, K, out_f32=True), True)[rows]
+    assert np.all(np.abs(y - Y) <= 4 * 2.0 ** -24 * np.abs(Y)), float(np.max(np.abs(y - Y)))
+    # bf16 with bias and GELU (the staged epilogue, ragged columns in the
+    # last tile column)
+    b = F.f64_to_bf16_rne(np.random.default_rng(3).normal(0, 0.5, N))
+    ref = G.linear_ref(Q.int8_decode(a[0][rows], a[1][rows]), Q.nvfp4_decode(*wq), b, gelu=True)
+    yb = _out(run_i8(a, wq, w8, M, N, K, bias=b, gelu=True), False)[rows]
+    assert rel_fro(yb, F.bf16_to_f64(F.f64_to_bf16_rne(ref))) <= TOL
+    # plain bf16 output with its |max|, then the NVFP4 output: the codes
+    # equal act_quant of the kernel's own bf16 output (given scale)
+    wts = dev(np.array([wq[2]], np.float32))
+    ws = qa.workspace(qa.qlinear_workspace(qa.INT8, M, N, K))
+    yy = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    slots = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, N))
+    slots.zero_()
+    amax = slots[:4096].view(t.int32)
+    qa.qlinear_int8_amax(dev(a[0]), dev(a[1]), None, None, wts, yy, amax, M, N, K, ws=ws, w8=w8)
+    t.cuda.synchronize()
+    yh = host(yy)
+    assert int(host(amax).astype(np.int64).max()) == \
+        int((yh.astype(np.uint32) & 0x7FFF).max()) << 16
+    if N % 16 == 0:
+        ts = np.float32(Q.nvfp4_tensor_scale(yh))
+        yq = t.empty((M, N // 2), dtype=t.uint8, device="cuda")
+        ys = t.empty((M, N // 16), dtype=t.uint8, device="cuda")
+        qa.qlinear_int8_q(dev(a[0]), dev(a[1]), None, None, wts, dev(np.array([ts], np.float32)),
+                          yq, ys, M, N, K, ws=ws, w8=w8)
+        t.cuda.synchronize()
+        oc, osc, _ = Q.nvfp4_encode(yh[rows], tscale=ts)
+        np.testing.assert_array_equal(host(yq)[rows], oc)
+        np.testing.assert_array_equal(host(ys)[rows], osc)
+
+
 def test_irregular_rows_refused():
     # rows whose non-zero group scales span 8 or more octaves have no
     # two-digit form: the set-up call counts them and refuses
