@@ -29,7 +29,11 @@
 // the tile's 16 KB of activations and 16 KB of plane rows are DMA'd
 // (buffer_load ... lds) into a 4-slot LDS ring, three units ahead; each wave
 // reads its fragments straight from the ring, one unit ahead.  Both kinds of
-// memory instruction are spread over the unit's 32 MFMAs.
+// memory instruction are spread over the unit's 32 MFMAs.  Two kernels:
+// qgemm_i8_kernel takes one tile per workgroup (and the K slices of a split
+// last round, and their fixup); qgemm_i8_persist, for short K loops over
+// more than one round of tiles, walks several tiles per workgroup through
+// one continuous stream of units.
 #include <hip/hip_ext.h>
 
 #include "qgemm_common.h"
