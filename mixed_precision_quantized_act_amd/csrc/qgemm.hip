@@ -558,8 +558,7 @@ qgemm_kernel(GemmArgs g, EpiArgs e) {
       row_scale[i] = g.a_rs[min<int64_t>(wave_row0 + 32 * i + c, e.M - 1)];
     rs[i] = I8 ? row_scale[i] * alpha : alpha;
   }
-  store_tile<kEpi, kFM>([&](int i, int j, int r) { return acc[i][j][r]; }, rs, wave_row0, wave_col0,
-                        smem + wave * 8192 * kPassTiles, e, lane);
+  store_tile<kEpi, kFM>(acc, rs, wave_row0, wave_col0, smem + wave * 8192 * kPassTiles, e, lane);
   }
 }
 

@@ -106,7 +106,8 @@ __host__ __device__ constexpr bool epi_staged(int k) {
 
 // Output of one wave's (32 FM) x 128 block: the wave's rows start at
 // wave_row0, its columns at wave_col0.  acc(i, j, r) gives the float32 sum
-// in register r of MFMA tile (i, j) as an MFMA issued W x A^T leaves it:
+// in register r of MFMA tile (i, j) as an MFMA issued W x A^T leaves it
+// (acc_in: the accumulator array, or a callable giving that sum):
 // lane (h, c) = (lane / 32, lane % 32) of tile (i, j) owns row 32 i + c
 // and, for q = 0..3, the 4 consecutive columns 32 j + 8 q + 4 h .. +3
 // (registers 4 q .. 4 q + 3); it is called where the value is consumed, so
@@ -116,9 +117,18 @@ __host__ __device__ constexpr bool epi_staged(int k) {
 // bias entry and are never stored.  stg: this wave's 8 KB (per pass of 32
 // rows) of idle LDS for the staged bf16 kinds.
 template <int kEpi, int FM, class Acc>
-__device__ __forceinline__ void store_tile(const Acc& acc, const float (&rs)[FM],
+__device__ __forceinline__ void store_tile(const Acc& acc_in, const float (&rs)[FM],
                                            int64_t wave_row0, int64_t wave_col0, uint8_t* stg,
                                            const EpiArgs& e, int lane) {
+  // Acc: the f32x16 [FM][4] accumulators themselves (read here: passing
+  // them through a caller's lambda measured a few spilled registers in the
+  // fp16 kernel) or a callable (i, j, r) -> float
+  auto acc = [&](int i, int j, int r) -> float {
+    if constexpr (std::is_array<Acc>::value)
+      return acc_in[i][j][r];
+    else
+      return acc_in(i, j, r);
+  };
   const int c = lane & 31, lh = lane >> 5;
   if constexpr (epi_staged(kEpi)) {
     // bf16 staged per 32-row slice through this wave's own 8 KB of the idle
