@@ -383,8 +383,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     a4 = qa.empty_nvfp4(M, F_, dev)
     a8 = qa.empty_int8_act(M, F_, dev)
     qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F_), dev)
-    gws = qa.workspace(max(qa.qlinear_workspace(f, M, N, K) for f in (qa.NVFP4, qa.INT8)
-                           for (N, K) in shapes), dev)
+    gws = qa.workspace(max([qa.qlinear_workspace(f, M, N, K) for f in (qa.NVFP4, qa.INT8)
+                            for (N, K) in shapes] +
+                           [qa.qlinear_routed_workspace(M, N, K) for (N, K) in shapes]), dev)
     rws = qa.workspace(qa.reduce_workspace(M * H), dev)
     ring = [[torch.empty((M, H), dtype=bf, device=dev) for _ in range(2)] for _ in range(L)]
     sums = torch.zeros((L, 4), dtype=torch.float64, device=dev)
@@ -544,9 +545,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
     def run_device(tau, delta, graph, routed=True):
         """DMPQ + TDC with the decisions made on the device
         (qa.decide_step) and every path enqueued under its gate: no host
-        sync inside a step (routed: the activation quantization and the Delta
-        ring calls take their format or slot from the gate byte in one launch
-        each; otherwise one gated launch per choice); graph: one step captured as a HIP graph and
+        sync inside a step (routed: the activation quantization, the GEMM and
+        the Delta ring calls take their format or slot from the gate byte in
+        one launch each; otherwise one gated launch per choice); graph: one step captured as a HIP graph and
         replayed.  Mean ms/step of steps 2.. (one sync around them)."""
         nonlocal outs
         if outs is None:
@@ -587,21 +588,9 @@ def stack_section(qa, torch, np, dev, stream, L=30, H=1920, F_=7680, M=17776, st
             else:
                 qa.act_quant_routed(flag, i16(xv), aq4, as4, a4[2], 0, qws, aq8, a8[1], M=M, K=K,
                                     ldx=ldx, stream=stream)
-            epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
-            with qa.gate(flag, qa.ROUTE_NVFP4):
-                if amax_out is not None:
-                    qa.qlinear_nvfp4_amax(aq4, as4, a4[2], q, sc, ts, y, amax_out, M, N, K,
-                                          epi=epi, ws=gws, stream=stream)
-                else:
-                    qa.qlinear_nvfp4(aq4, as4, a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=gws,
-                                     stream=stream)
-            with qa.gate(flag, qa.ROUTE_INT8):
-                if amax_out is not None:
-                    qa.qlinear_int8_amax(aq8, a8[1], q, sc, ts, y, amax_out, M, N, K, epi=epi,
-                                         ws=gws, stream=stream, w8=w8)
-                else:
-                    qa.qlinear_int8(aq8, a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=gws,
-                                    stream=stream, w8=w8)
+            qa.qlinear_routed(flag, aq4, as4, a4[2], aq8, a8[1], q, sc, ts, w8, y, M, N, K,
+                              epi=qa.EPI_GELU_TANH if gelu else qa.EPI_NONE, y_amax=amax_out,
+                              ws=gws, stream=stream)
 
         def step(stream):
             qa.decide_step(sums, alpha_d, beta_d, tau, delta, L, J, t_ctr, bstate, d_dev, blk,

@@ -113,7 +113,7 @@ int act_quant(qa_fmt fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  * gate byte of qa_decide_step: (*route & 1) NVFP4 into (q4, s4, *ts4) with
  * flags4 and ws4 as for act_quant (QA_TSCALE_GIVEN or QA_AMAX_GIVEN: the
  * encoder alone; neither: a tensor-max launch first, which also runs only
- * for NVFP4); (*route & 2) INT8 into (q8, s8); 0: nothing.  The outputs of
+ * for NVFP4); otherwise (*route & 2) INT8 into (q8, s8); 0: nothing.  The outputs of
  * the format not chosen are left as they were.  Arguments as for act_quant
  * (both formats' buffers required); the outputs overlap neither each other
  * nor x. */
@@ -271,6 +271,34 @@ int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
                       int64_t N, int64_t K, const uint16_t* bias, void* y, int64_t ldy,
                       qa_epi epi, uint32_t* y_amax, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* qlinear_routed: the linear in the activation format that the device byte
+ * *route selects, with one GEMM launch for both formats, for a timestep
+ * enqueued (or captured in a graph) before its decisions are known
+ * (6Bit-Diffusion, Fig. 2 caption: each linear's activation format is
+ * chosen per timestep).  *route is a linear gate byte of qa_decide_step:
+ * (*route & 1) qlinear_nvfp4 on (a_q4, a_s4, a_ts4); otherwise (*route & 2)
+ * qlinear_int8 on (a_q8, a_s8) with w8 (the integer kernel); 0: nothing,
+ * y and y_amax left as they were.  The outputs are those of the call the
+ * byte selects, bit for bit.  Both formats' operands are required (w_q,
+ * w_s for NVFP4, w8 for INT8, w_ts for both); y bf16 [M][ldy], 16-byte
+ * aligned, ldy % 4 == 0 (QA_EUNSUPPORTED otherwise); y_amax: NULL or as
+ * for qlinear_*_amax.  K % 16 == 0.  ws: qlinear_routed_workspace(M, N, K)
+ * bytes (0 if the shape is rejected) split the last round of tiles along K
+ * as the plain calls do; at least qlinear_workspace(QA_NVFP4, ...) without
+ * the split.  Launches: the NVFP4 scale re-layout (runs only for NVFP4;
+ * none at most 256 tiles of 256x256 with K % 64 == 0, where the scales
+ * are read in place), the whole tiles of either format, and, when the last
+ * round is split, each format's K slices and fixup (each runs only for its
+ * format).  Where the INT8 whole tiles take the persistent kernel (more
+ * than 256 tiles of 256x128, K / 64 even and 6..64), each format's whole
+ * tiles launch on their own instead (each runs only for its format). */
+size_t qlinear_routed_workspace(int64_t M, int64_t N, int64_t K);
+int qlinear_routed(const uint8_t* route, const uint8_t* a_q4, const uint8_t* a_s4,
+                   const float* a_ts4, const int8_t* a_q8, const float* a_s8, const uint8_t* w_q,
+                   const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M, int64_t N,
+                   int64_t K, const uint16_t* bias, uint16_t* y, int64_t ldy, qa_epi epi,
+                   uint32_t* y_amax, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* act_quant of x followed by the matching qlinear_* (one layer).  For
  * NVFP4 the tensor scale is computed from x (flags may hold

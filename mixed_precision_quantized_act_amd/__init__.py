@@ -14,7 +14,8 @@ from ._lib import (AMAX_GIVEN, BLK_RUN0, BLK_RUN1, BLK_SKIP0, BLK_SKIP1, EPI_GEL
                    int8_weight_planes_bytes, int8_weight_planes_count, lib, qlinear,
                    qlinear_int8, qlinear_int8_acc, qlinear_int8_noalloc,
                    qlinear_int8_amax, qlinear_int8_q, qlinear_layer_workspace, qlinear_nvfp4,
-                   qlinear_nvfp4_amax, qlinear_nvfp4_q, qlinear_workspace, reduce_workspace,
+                   qlinear_nvfp4_amax, qlinear_nvfp4_q, qlinear_routed, qlinear_routed_workspace,
+                   qlinear_workspace, reduce_workspace,
                    rel_err, rel_err_from_sums, rel_l2_from_sums, set_gate, set_gemm_events,
                    strerror, tdc_apply, tdc_apply_amax, tdc_apply_ring, tdc_decide, tdc_decide_cos,
                    tdc_update, tdc_update_ring)

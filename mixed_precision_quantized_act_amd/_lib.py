@@ -59,6 +59,9 @@ _SIGS = {
                                _I64, _I64, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P, _SZ, _P]),
     "act_quant_routed": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _P, ctypes.c_uint32, _P,
                                         _SZ, _P, _P, _P]),
+    "qlinear_routed_workspace": (_SZ, [_I64, _I64, _I64]),
+    "qlinear_routed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                      _P, _P, _I64, ctypes.c_int, _P, _P, _SZ, _P]),
     "tdc_update_ring": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tdc_apply_ring": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "reduce_workspace": (_SZ, [_I64]),
@@ -276,6 +279,22 @@ def act_quant_routed(route, x, q4, s4, ts4, flags4, ws4, q8, s8, M=None, K=None,
     _check("act_quant_routed", lib().act_quant_routed(
         _ptr(route), _ptr(x), M, K, ldx, _ptr(q4), _ptr(s4), _ptr(ts4), flags4, _ptr(ws4),
         _nbytes(ws4), _ptr(q8), _ptr(s8), _stream(stream)))
+
+
+def qlinear_routed_workspace(M, N, K):
+    return lib().qlinear_routed_workspace(M, N, K)
+
+
+def qlinear_routed(route, a_q4, a_s4, a_ts4, a_q8, a_s8, w_q, w_s, w_ts, w8, y, M, N, K,
+                   bias=None, epi=EPI_NONE, y_amax=None, ws=None, ldy=None, stream=None):
+    """The linear in the format the device byte route[0] selects (1 NVFP4
+    on (a_q4, a_s4, a_ts4), 2 INT8 on (a_q8, a_s8) with w8, 0 nothing):
+    one GEMM launch for both formats; bf16 y, y_amax as for *_amax."""
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("qlinear_routed", lib().qlinear_routed(
+        _ptr(route), _ptr(a_q4), _ptr(a_s4), _ptr(a_ts4), _ptr(a_q8), _ptr(a_s8), _ptr(w_q),
+        _ptr(w_s), _ptr(w_ts), _ptr(w8), M, N, K, _ptr(bias), _ptr(y), ldy, epi, _ptr(y_amax),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def tdc_update_ring(blk, x_in, x_out, ring0, ring1, sums4, ws, n=None, stream=None):

@@ -365,6 +365,46 @@ int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
   return s;
 }
 
+// ------------------------------------------------------- routed linear --
+
+size_t qlinear_routed_workspace(int64_t M, int64_t N, int64_t K) {
+  if (check_mk(M, K) || check_nk(M, N, K) || K % 16) return 0;
+  const size_t a = nvfp4_gemm_ws_bytes(M, N, K), b = int8_i8_gemm_ws_bytes(M, N, K);
+  return a > b ? a : b;
+}
+
+int qlinear_routed(const uint8_t* route, const uint8_t* a_q4, const uint8_t* a_s4,
+                   const float* a_ts4, const int8_t* a_q8, const float* a_s8, const uint8_t* w_q,
+                   const uint8_t* w_s, const float* w_ts, const void* w8, int64_t M, int64_t N,
+                   int64_t K, const uint16_t* bias, uint16_t* y, int64_t ldy, qa_epi epi,
+                   uint32_t* y_amax, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!route || !a_q4 || !a_s4 || !a_ts4 || !a_q8 || !a_s8 || !w_q || !w_s || !w_ts || !w8)
+    return QA_EINVAL;
+  if (int s = check_linear(M, N, K, y, ldy, QA_OUT_BF16, epi)) return s;
+  if (K % 16) return QA_ESHAPE;
+  if (!aligned16(a_q4) || !aligned16(a_q8) || !aligned16(w_q)) return QA_EALIGN;
+  if (reinterpret_cast<uintptr_t>(w8) & 255u) return QA_EALIGN;
+  GemmOut o = {y, ldy, 0, epi == QA_EPI_GELU_TANH, bias};
+  o.y_amax = y_amax;
+  if (!gemm_out_staged(o)) return QA_EUNSUPPORTED;
+  {
+    const size_t need = nvfp4_gemm_ws_need(M, N, K, w_s);
+    if (ws_bytes < need || (need && !ws)) return QA_EWORKSPACE;
+  }
+  if (!aligned16(ws)) return QA_EALIGN;
+  const size_t ybytes = M && N ? (size_t)((M - 1) * ldy + N) * 2 : 0;
+  if (y_amax && M > 0 && N > 0)
+    if (int s = check_amax_out(o, y_amax, y, ybytes, ws, ws_bytes)) return s;
+  if (overlap(y, ybytes, a_q4, (size_t)(M * K / 2)) || overlap(y, ybytes, a_q8, (size_t)(M * K)) ||
+      overlap(y, ybytes, w_q, (size_t)(N * K / 2)) ||
+      overlap(y, ybytes, w8, int8_planes_bytes(N, K)) || overlap(y, ybytes, ws, ws_bytes) ||
+      overlap(y, ybytes, route, 1))
+    return QA_EALIAS;
+  if (M == 0 || N == 0) return QA_OK;
+  return hip_status(launch_routed_gemm(route, a_q4, a_s4, a_ts4, a_q8, a_s8, w_q, w_s, w_ts, w8,
+                                       M, N, K, o, ws, ws_bytes, stream));
+}
+
 // NVFP4 output of the linear (activation quantization of its consumer,
 // fused into the producing GEMM's epilogue)
 static int check_qout(int64_t M, int64_t N, int64_t K, qa_epi epi, const float* y_ts,

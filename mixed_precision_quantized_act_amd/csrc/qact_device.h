@@ -97,7 +97,11 @@ __device__ __forceinline__ int e2m1_twice(uint32_t c) {
 
 // True when the call's gate is closed: its kernels then return at once.
 // (One uniform byte load; every kernel of a gated call checks it first.)
-__device__ __forceinline__ bool gated_off(Gate g) { return g.flags && (*g.flags & g.bits) == 0u; }
+__device__ __forceinline__ bool gated_off(Gate g) {
+  if (!g.flags) return false;
+  const uint32_t v = *g.flags;
+  return (v & g.bits) == 0u || (v & g.veto) != 0u;
+}
 
 // Wave-level (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {

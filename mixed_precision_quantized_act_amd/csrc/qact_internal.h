@@ -10,11 +10,13 @@
 namespace qact {
 
 // Device-side gate of a call: every kernel of the call reads the byte
-// *flags on the device and does nothing unless (*flags & bits) != 0.
-// flags == nullptr: no gate.  Set per host thread through qa_set_gate.
+// *flags on the device and does nothing unless (*flags & bits) != 0 and
+// (*flags & veto) == 0.  flags == nullptr: no gate.  Set per host thread
+// through qa_set_gate (veto 0); a routed call builds its own per format.
 struct Gate {
   const uint8_t* flags;
   uint32_t bits;
+  uint32_t veto = 0u;
 };
 Gate current_gate();
 
@@ -110,6 +112,14 @@ hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* 
                                const GemmOut& o, void* ws, size_t ws_bytes, int32_t* acc_hi,
                                int32_t* acc_lo, hipStream_t stream);
 void set_i8_gemm_events(hipEvent_t before, hipEvent_t after);
+// the linear in the format the device byte *route selects (kRouteNvfp4:
+// the NVFP4 operands; kRouteInt8: the INT8 operands with w8), whole tiles
+// in one launch; bf16 staged outputs only (the ABI checks)
+hipError_t launch_routed_gemm(const uint8_t* route, const uint8_t* a_q4, const uint8_t* a_s4,
+                              const float* a_ts4, const int8_t* a_q8, const float* a_s8,
+                              const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                              const void* w8, int64_t M, int64_t N, int64_t K, const GemmOut& o,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- Gamma / Temporal Delta Cache (tdc.hip)
 // qlinear_int8's argument checks other than those of its workspace

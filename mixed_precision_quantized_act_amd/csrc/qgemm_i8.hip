@@ -37,6 +37,7 @@
 #include <hip/hip_ext.h>
 
 #include "qgemm_common.h"
+#include "qgemm_f16.h"
 
 namespace qact {
 
@@ -331,17 +332,17 @@ __device__ __forceinline__ void i8_epilogue(const i32x16 (&acc)[kFM][kFN], const
 }  // namespace
 
 
+// The per-tile kernel's body: workgroup `bid` of a launch in mode kMode,
+// with the launch's LDS (kSmem bytes, 16-byte aligned) at smem.
 template <int kEpi, int kMode>
-__global__ void __launch_bounds__(kThreads, 1)
-qgemm_i8_kernel(I8Args g, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+__device__ __forceinline__ void i8_tile_body(const I8Args& g, const EpiArgs& e, uint8_t* smem,
+                                             int bid) {
   if (gated_off(g.gate)) return;
 
   // tile of this workgroup: XCD-aware order as in the fp16 kernel (each
   // XCD a contiguous range of logical tiles, grouped 8 tile-rows at a time)
   TileWork tw;
-  if (!tile_work(kMode, (int)blockIdx.x, g.main_tiles, g.splits, g.split_units, g.units, tw))
-    return;
+  if (!tile_work(kMode, bid, g.main_tiles, g.splits, g.split_units, g.units, tw)) return;
   const int logical = tw.logical, slice = tw.slice, u_begin = tw.u_begin, u_count = tw.u_count;
   int tm, tn;
   tile_coords(logical, g.mt, g.nt, 8, tm, tn);
@@ -534,6 +535,13 @@ qgemm_i8_kernel(I8Args g, EpiArgs e) {
   }
 }
 
+template <int kEpi, int kMode>
+__global__ void __launch_bounds__(kThreads, 1)
+qgemm_i8_kernel(I8Args g, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  i8_tile_body<kEpi, kMode>(g, e, smem, (int)blockIdx.x);
+}
+
 // Persistent whole-tile kernel for short K loops: a grid of one workgroup
 // per CU, each taking the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
 // the whole-tile order (gridDim.x a multiple of 8, so that a workgroup
@@ -694,6 +702,27 @@ qgemm_i8_persist(I8Args g, EpiArgs e) {
   wait_vm<0>();   // no DMA into LDS outlives the workgroup
 }
 
+// Routed linear: the whole tiles of either format in one launch, the
+// format read from the device byte *route (kRouteNvfp4: the fp16-MFMA
+// NVFP4 kernel's body; otherwise kRouteInt8: the per-tile integer kernel's
+// body; neither: nothing), for a step enqueued or captured before its
+// decisions are known.  The grid covers the larger of the two whole-tile
+// grids; each body takes only the workgroups of its own.  The LDS holds
+// either body's.
+template <int kEpi>
+__global__ void __launch_bounds__(kThreads, 1)
+qgemm_routed_kernel(GemmArgs gf, I8Args gi, EpiArgs e, const uint8_t* route) {
+  constexpr int kF16 = f16k::Raw<false>::kSmem;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kF16 > kSmem ? kF16 : kSmem];
+  const uint32_t r = *route;
+  const int bid = (int)blockIdx.x;
+  if (r & kRouteNvfp4) {
+    if (bid < gf.grid_main) f16k::qgemm_body<false, kEpi, kWhole>(gf, e, smem, bid);
+  } else if (r & kRouteInt8) {
+    if (bid < gi.grid_main) i8_tile_body<kEpi, kWhole>(gi, e, smem, bid);
+  }
+}
+
 // ------------------------------------------------------------------ host --
 
 namespace {
@@ -720,15 +749,17 @@ void launch_mode(int grid, hipEvent_t before, hipEvent_t after, const I8Args& g,
 // tiles (measured 5-6 % faster at K = 1920, 1.6 % at 3072, 1 % slower at
 // 7680, where the static assignment of tiles to workgroups costs more)
 constexpr int kPersistMaxUnits = 64;
+bool persist_fits(const I8Args& g) {
+  return g.main_tiles && g.units % 2 == 0 && g.units >= 6 && g.units <= kPersistMaxUnits &&
+         g.grid_main > kCUs;
+}
 
 template <int kEpi>
 void launch_one(const I8Args& g, const EpiArgs& e, hipStream_t st) {
   const int tail = g.mt * g.nt - g.main_tiles;
   bool persist = false;
-  if constexpr (kEpi != kEpiAcc)
-    persist = g.units % 2 == 0 && g.units >= 6 && g.units <= kPersistMaxUnits &&
-              g.grid_main > kCUs;
-  if (g.main_tiles && persist) {
+  if constexpr (kEpi != kEpiAcc) persist = persist_fits(g);
+  if (persist) {
     if constexpr (kEpi != kEpiAcc) {
       hipEvent_t after = tail ? nullptr : g_ev_after;
       if (g_ev_before || after)
@@ -758,11 +789,10 @@ size_t int8_i8_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return (size_t)p.tail * p.splits * kPartTile * 4;
 }
 
-hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* w8,
-                               const float* w_ts, int64_t M, int64_t N, int64_t K,
-                               const GemmOut& o, void* ws, size_t ws_bytes, int32_t* acc_hi,
-                               int32_t* acc_lo, hipStream_t st) {
-  if (M == 0 || N == 0) return hipSuccess;
+// the integer kernel's arguments (split: the K split of a partly filled
+// last round, when the workspace holds it)
+static I8Args i8_args(const int8_t* a_q, const float* a_s, const void* w8, const float* w_ts,
+                      int64_t M, int64_t N, int64_t K, void* ws, bool split) {
   I8Args g = {};
   g.gate = current_gate();
   g.a = reinterpret_cast<const uint8_t*>(a_q);
@@ -776,14 +806,23 @@ hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* 
   g.units = (int)units_of(K);
   g.mt = (int)((M + kTileM - 1) / kTileM);
   g.nt = (int)nt;
-  const bool split = acc_hi == nullptr && ws_bytes >= int8_i8_gemm_ws_bytes(M, N, K) &&
-                     int8_i8_gemm_ws_bytes(M, N, K) > 0;
   const SplitPlan p = split ? split_plan(M, N, K) : SplitPlan{g.mt * g.nt, 0, 1, g.units};
   g.main_tiles = p.main_tiles;
   g.grid_main = 8 * ((p.main_tiles + 7) / 8);
   g.splits = p.splits;
   g.split_units = p.split_units;
   if (p.tail) g.part = static_cast<int32_t*>(ws);
+  return g;
+}
+
+hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* w8,
+                               const float* w_ts, int64_t M, int64_t N, int64_t K,
+                               const GemmOut& o, void* ws, size_t ws_bytes, int32_t* acc_hi,
+                               int32_t* acc_lo, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const bool split = acc_hi == nullptr && ws_bytes >= int8_i8_gemm_ws_bytes(M, N, K) &&
+                     int8_i8_gemm_ws_bytes(M, N, K) > 0;
+  I8Args g = i8_args(a_q, a_s, w8, w_ts, M, N, K, ws, split);
   g.acc_hi = acc_hi;
   g.acc_lo = acc_lo;
   const int vec = (reinterpret_cast<uintptr_t>(o.y) % 16 == 0) && (o.ldy % 4 == 0);
@@ -812,6 +851,72 @@ hipError_t launch_int8_i8_gemm(const int8_t* a_q, const float* a_s, const void* 
     default: launch_one<kEpiGeneral>(g, e, st); break;
   }
   return hipGetLastError();
+}
+
+// The routed linear: the NVFP4 scale re-layout (run only for kRouteNvfp4;
+// none when the scales are read in place), one routed launch of the whole
+// tiles, then the K slices and fixups of either format when its last round
+// is split (each run only for its format).  Where the INT8 whole tiles
+// take the persistent kernel (more than one round of short-K tiles), the
+// per-tile body of a routed launch is the slower one and one launch more
+// costs little beside the GEMM: there each format's own launches run, each
+// under its part of the route.  Bf16 staged outputs only (the caller
+// checks).
+hipError_t launch_routed_gemm(const uint8_t* route, const uint8_t* a_q4, const uint8_t* a_s4,
+                              const float* a_ts4, const int8_t* a_q8, const float* a_s8,
+                              const uint8_t* w_q, const uint8_t* w_s, const float* w_ts,
+                              const void* w8, int64_t M, int64_t N, int64_t K, const GemmOut& o,
+                              void* ws, size_t ws_bytes, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmArgs gf;
+  EpiArgs e;
+  hipError_t err = nvfp4_gemm_prepare(a_q4, a_s4, a_ts4, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes,
+                                      Gate{route, kRouteNvfp4}, st, gf, e);
+  if (err != hipSuccess) return err;
+  const bool split = ws_bytes >= int8_i8_gemm_ws_bytes(M, N, K) &&
+                     int8_i8_gemm_ws_bytes(M, N, K) > 0;
+  I8Args gi = i8_args(a_q8, a_s8, w8, w_ts, M, N, K, ws, split);
+  gi.gate = Gate{route, kRouteInt8, kRouteNvfp4};     // a byte with both bits: NVFP4 only
+  // the whole tiles: the kernel reads the route itself
+  GemmArgs gfm = gf;
+  I8Args gim = gi;
+  gfm.gate = Gate{nullptr, 0u};
+  gim.gate = Gate{nullptr, 0u};
+  if (!gfm.main_tiles) gfm.grid_main = 0;
+  if (!gim.main_tiles) gim.grid_main = 0;
+  const int grid = gfm.grid_main > gim.grid_main ? gfm.grid_main : gim.grid_main;
+  const int kind = (o.bias ? (o.gelu ? kEpiStagedBiasGelu : kEpiStagedBias)
+                           : (o.gelu ? kEpiStagedGelu : kEpiPlain)) +
+                   (o.y_amax ? kEpiAmax : 0);
+  const bool separate = persist_fits(gi);
+  auto go = [&](auto kc) {
+    constexpr int kEpi = decltype(kc)::value;
+    if (separate) {
+      launch_one<kEpi>(gi, e, st);
+      return;
+    }
+    if (grid)
+      hipLaunchKernelGGL((qgemm_routed_kernel<kEpi>), dim3(grid), dim3(kThreads), 0, st, gfm,
+                         gim, e, route);
+    const int tail = gi.mt * gi.nt - gi.main_tiles;
+    if (tail) {
+      launch_mode<kEpiPlain, kSlice>(tail * gi.splits, nullptr, nullptr, gi, e, st);
+      launch_mode<kEpi, kFixup>(tail, nullptr, nullptr, gi, e, st);
+    }
+  };
+  switch (kind) {
+    case kEpiPlain: go(std::integral_constant<int, kEpiPlain>()); break;
+    case kEpiStagedBias: go(std::integral_constant<int, kEpiStagedBias>()); break;
+    case kEpiStagedGelu: go(std::integral_constant<int, kEpiStagedGelu>()); break;
+    case kEpiStagedBiasGelu: go(std::integral_constant<int, kEpiStagedBiasGelu>()); break;
+    case kEpiAmax + kEpiPlain: go(std::integral_constant<int, kEpiAmax + kEpiPlain>()); break;
+    case kEpiAmax + kEpiStagedBias: go(std::integral_constant<int, kEpiAmax + kEpiStagedBias>()); break;
+    case kEpiAmax + kEpiStagedGelu: go(std::integral_constant<int, kEpiAmax + kEpiStagedGelu>()); break;
+    default: go(std::integral_constant<int, kEpiAmax + kEpiStagedBiasGelu>()); break;
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return nvfp4_gemm_launch(gf, e, st, !separate);
 }
 
 }  // namespace qact

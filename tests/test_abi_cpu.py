@@ -173,6 +173,35 @@ def test_routed_and_stage_validation():
     assert _status("qa_test_stage_ab", 0, 1, 1, ctypes.c_void_p(0x100002), A[1], None) == -3
 
 
+def test_routed_linear_validation():
+    # qlinear_routed: route byte and both formats' operands required; bf16
+    # staged output only; K % 16; alignment; the NVFP4 workspace at least;
+    # the output must not overlap operands, workspace or the route byte
+    A = [ctypes.c_void_p(0x1000000 * (i + 1)) for i in range(16)]
+    M, N, K = 64, 256, 256
+    ok = [A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7], A[8], A[9], M, N, K, None, A[10], N, 0,
+          None, A[11], 1 << 24, None]
+    assert qa.lib().qlinear_routed_workspace(M, N, K) > 0
+    assert qa.lib().qlinear_routed_workspace(M, N, 24) == 0
+    for i in range(10):                                   # any missing operand
+        bad = list(ok); bad[i] = None
+        assert _status("qlinear_routed", *bad) == -1, i
+    bad = list(ok); bad[12] = 24
+    assert _status("qlinear_routed", *bad) == -2           # K % 16
+    bad = list(ok); bad[15] = N - 1
+    assert _status("qlinear_routed", *bad) == -2           # ldy < N
+    bad = list(ok); bad[9] = ctypes.c_void_p(0x1000000 * 10 + 16)
+    assert _status("qlinear_routed", *bad) == -3           # w8 256-byte aligned
+    bad = list(ok); bad[14] = ctypes.c_void_p(0x1000000 * 11 + 2)
+    assert _status("qlinear_routed", *bad) == -4           # y not 16-byte aligned: unsupported
+    bad = list(ok); bad[19] = 0
+    assert _status("qlinear_routed", *bad) == -5           # no workspace
+    bad = list(ok); bad[14] = A[1]
+    assert _status("qlinear_routed", *bad) == -7           # y on a_q4
+    bad = list(ok); bad[0] = ctypes.c_void_p(0x1000000 * 11 + 64)
+    assert _status("qlinear_routed", *bad) == -7           # route byte inside y
+
+
 def test_strerror_covers_codes():
     for s in range(-8, 1):
         assert qa.strerror(s) != "unknown status"

@@ -125,3 +125,71 @@ def test_tdc_ring_calls():
                 assert np.all(host(out) == 0x1234) and np.all(host(s2) == -1.0)
                 if with_amax:
                     assert not host(amax).any()
+
+
+# qlinear_routed against the plain call of the chosen format: small, with
+# bias + GELU + the output |max| and ragged N, a K-split last round in both
+# formats (only the slices and fixups launch), many tiles with ragged M and
+# N in one routed launch (7 units: no persistent INT8 kernel), and many
+# short-K tiles, where the INT8 whole tiles take the persistent kernel and
+# each format launches on its own
+ROUTED_SHAPES = [(300, 256, 384, False, False, False), (300, 200, 192, True, True, True),
+                 (600, 704, 3840, False, False, True), (2000, 1000, 448, False, True, True),
+                 (4452, 1960, 1920, False, True, False), (4452, 3840, 1920, True, True, True)]
+
+
+@pytest.mark.parametrize("route", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K,bias,gelu,amax", ROUTED_SHAPES)
+def test_qlinear_routed(M, N, K, bias, gelu, amax, route):
+    qa, t = _qa(), torch()
+    x = dev(synth.activations(13, M, K, "normal", 4, 20.0))
+    w = dev(synth.weight(13, 0, N, K))
+    a4 = qa.empty_nvfp4(M, K)
+    qa.act_quant(qa.NVFP4, x, a4[0], a4[1], a4[2], 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K)))
+    a8 = qa.empty_int8_act(M, K)
+    qa.act_quant(qa.INT8, x, a8[0], a8[1])
+    wq = qa.empty_nvfp4(N, K)
+    qa.act_quant(qa.NVFP4, w, wq[0], wq[1], wq[2], 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K)))
+    w8 = qa.empty_int8_planes(N, K)
+    assert qa.int8_weight_planes(wq[0], wq[1], w8, N, K) == 0
+    b = dev(np.random.default_rng(5).normal(0, 0.5, N).astype(np.float32)).to(t.bfloat16) \
+        if bias else None
+    epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
+    ws = qa.workspace(qa.qlinear_routed_workspace(M, N, K))
+    slots = t.zeros(1024, dtype=t.int32, device="cuda")
+    # reference: the plain call of the format the byte selects
+    ref = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    ref_slots = t.zeros(1024, dtype=t.int32, device="cuda")
+    fmt = 1 if route & 1 else (2 if route & 2 else 0)
+    if fmt == 1:
+        if amax:
+            qa.qlinear_nvfp4_amax(a4[0], a4[1], a4[2], wq[0], wq[1], wq[2], ref, ref_slots, M, N, K,
+                                  bias=b, epi=epi, ws=ws)
+        else:
+            qa.qlinear_nvfp4(a4[0], a4[1], a4[2], wq[0], wq[1], wq[2], ref, M, N, K, bias=b,
+                             epi=epi, ws=ws)
+    elif fmt == 2:
+        if amax:
+            qa.qlinear_int8_amax(a8[0], a8[1], None, None, wq[2], ref, ref_slots, M, N, K, bias=b,
+                                 epi=epi, ws=ws, w8=w8)
+        else:
+            qa.qlinear_int8(a8[0], a8[1], None, None, wq[2], ref, M, N, K, bias=b, epi=epi, ws=ws,
+                            w8=w8)
+    t.cuda.synchronize()
+    y = t.full((M, N), -3.0, dtype=t.bfloat16, device="cuda")
+    qa.qlinear_routed(_byte(route), a4[0], a4[1], a4[2], a8[0], a8[1], wq[0], wq[1], wq[2], w8,
+                      y, M, N, K, bias=b, epi=epi, y_amax=slots if amax else None, ws=ws)
+    t.cuda.synchronize()
+    if fmt == 0:
+        assert bool((y == -3.0).all())
+        assert int(slots.abs().max()) == 0
+        return
+    assert t.equal(y.view(t.int16), ref.view(t.int16))
+    if amax:
+        # the output's |max| (how it spreads over the 1024 words follows the
+        # launch's workgroups)
+        assert int(slots.max()) == int(ref_slots.max())
+        yb = host(y.view(t.int16)).astype(np.uint32) & 0x7FFF
+        assert int(slots.max()) == int(yb.max()) << 16

@@ -82,7 +82,9 @@ class _Stack:
                 w = (t.randn((N, K), generator=gen, device="cuda") * 0.02).to(t.bfloat16)
                 q, sc, ts = qa.empty_nvfp4(N, K)
                 qa.act_quant(qa.NVFP4, w.view(t.int16), q, sc, ts, 0, qw)
-                lay.append((q, sc, ts, N, K))
+                w8 = qa.empty_int8_planes(N, K)
+                assert qa.int8_weight_planes(q, sc, w8, N, K) == 0
+                lay.append((q, sc, ts, N, K, w8))
             self.layers.append(lay)
         bf = t.bfloat16
         self.qkv = t.empty((M, 3 * H), dtype=bf, device="cuda")
@@ -93,8 +95,9 @@ class _Stack:
         self.a4 = qa.empty_nvfp4(M, F)
         self.a8 = qa.empty_int8_act(M, F)
         self.qws = qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, F))
-        self.gws = qa.workspace(max(qa.qlinear_workspace(f, M, N, K) for f in (qa.NVFP4, qa.INT8)
-                                    for (N, K) in SHAPES))
+        self.gws = qa.workspace(max([qa.qlinear_workspace(f, M, N, K) for f in (qa.NVFP4, qa.INT8)
+                                     for (N, K) in SHAPES] +
+                                    [qa.qlinear_routed_workspace(M, N, K) for (N, K) in SHAPES]))
         self.rws = qa.workspace(qa.reduce_workspace(M * H))
         self.ring = [[t.zeros((M, H), dtype=bf, device="cuda") for _ in range(2)] for _ in range(L)]
         self.outs = [t.empty((M, H), dtype=bf, device="cuda") for _ in range(L)]
@@ -120,7 +123,7 @@ class _Stack:
 
     def linear(self, fmt, x, ldx, lay, y, gelu):
         qa, t = self.qa, self.t
-        q, sc, ts, N, K = lay
+        q, sc, ts, N, K, w8 = lay
         xv = t.as_strided(x, (M, K), (ldx, 1)).view(t.int16)
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         if fmt == 0:
@@ -131,11 +134,11 @@ class _Stack:
         else:
             aq = self.a8[0].view(-1)[: M * K].view(M, K)
             qa.act_quant(qa.INT8, xv, aq, self.a8[1], M=M, K=K, ldx=ldx)
-            qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
+            qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws, w8=w8)
 
     def gemm(self, fmt, lay, y, gelu, K):
         qa = self.qa
-        q, sc, ts, N, _ = lay
+        q, sc, ts, N, _, w8 = lay
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
         if fmt == 0:
             aq = self.a4[0].view(-1)[: M * K // 2].view(M, K // 2)
@@ -143,11 +146,11 @@ class _Stack:
             qa.qlinear_nvfp4(aq, asc, self.a4[2], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
         else:
             aq = self.a8[0].view(-1)[: M * K].view(M, K)
-            qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws)
+            qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws, w8=w8)
 
     def routed_linear(self, flag, x, ldx, lay, y, gelu):
-        """One act_quant launch in the format the linear's flag selects, then
-        each format's GEMM under its gate."""
+        """One act_quant launch and one GEMM launch in the format the linear's
+        flag selects."""
         qa, t = self.qa, self.t
         K = lay[4]
         xv = t.as_strided(x, (M, K), (ldx, 1)).view(t.int16)
@@ -156,9 +159,9 @@ class _Stack:
         aq8 = self.a8[0].view(-1)[: M * K].view(M, K)
         qa.act_quant_routed(flag, xv, aq4, as4, self.a4[2], 0, self.qws, aq8, self.a8[1], M=M,
                             K=K, ldx=ldx)
-        for fmt, bit in ((0, qa.ROUTE_NVFP4), (1, qa.ROUTE_INT8)):
-            with qa.gate(flag, bit):
-                self.gemm(fmt, lay, y, gelu, K)
+        q, sc, ts, N, _, w8 = lay
+        qa.qlinear_routed(flag, aq4, as4, self.a4[2], aq8, self.a8[1], q, sc, ts, w8, y, M, N, K,
+                          epi=qa.EPI_GELU_TANH if gelu else qa.EPI_NONE, ws=self.gws)
 
     def block(self, l, cur, out, fmts, gated, routed=False):
         """The compute path of block l (linears in formats fmts, or both
