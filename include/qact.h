@@ -292,7 +292,9 @@ int qlinear_int8_amax(const int8_t* a_q, const float* a_s, const uint8_t* w_q,
  * round is split, each format's K slices and fixup (each runs only for its
  * format).  Where the INT8 whole tiles take the persistent kernel (more
  * than 256 tiles of 256x128, K / 64 even and 6..64), each format's whole
- * tiles launch on their own instead (each runs only for its format). */
+ * tiles launch on their own instead (each runs only for its format).  A
+ * gate set with qa_set_gate applies to every one of these launches as
+ * well. */
 size_t qlinear_routed_workspace(int64_t M, int64_t N, int64_t K);
 int qlinear_routed(const uint8_t* route, const uint8_t* a_q4, const uint8_t* a_s4,
                    const float* a_ts4, const int8_t* a_q8, const float* a_s8, const uint8_t* w_q,

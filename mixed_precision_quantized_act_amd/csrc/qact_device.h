@@ -100,7 +100,8 @@ __device__ __forceinline__ int e2m1_twice(uint32_t c) {
 __device__ __forceinline__ bool gated_off(Gate g) {
   if (!g.flags) return false;
   const uint32_t v = *g.flags;
-  return (v & g.bits) == 0u || (v & g.veto) != 0u;
+  if ((v & g.bits) == 0u || (v & g.veto) != 0u) return true;
+  return g.flags2 && (*g.flags2 & g.bits2) == 0u;
 }
 
 // Wave-level (64 lanes) reductions.

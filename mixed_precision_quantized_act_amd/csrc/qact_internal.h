@@ -11,12 +11,16 @@ namespace qact {
 
 // Device-side gate of a call: every kernel of the call reads the byte
 // *flags on the device and does nothing unless (*flags & bits) != 0 and
-// (*flags & veto) == 0.  flags == nullptr: no gate.  Set per host thread
-// through qa_set_gate (veto 0); a routed call builds its own per format.
+// (*flags & veto) == 0, and, when flags2 is set, (*flags2 & bits2) != 0.
+// flags == nullptr: no gate.  Set per host thread through qa_set_gate
+// (veto 0, no flags2); a routed call builds its own per format, with the
+// thread's gate as the second byte.
 struct Gate {
   const uint8_t* flags;
   uint32_t bits;
   uint32_t veto = 0u;
+  const uint8_t* flags2 = nullptr;
+  uint32_t bits2 = 0u;
 };
 Gate current_gate();
 

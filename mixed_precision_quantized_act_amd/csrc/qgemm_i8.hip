@@ -868,20 +868,26 @@ hipError_t launch_routed_gemm(const uint8_t* route, const uint8_t* a_q4, const u
                               const void* w8, int64_t M, int64_t N, int64_t K, const GemmOut& o,
                               void* ws, size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  // every launch also honours the thread's gate (qa_set_gate), as a second
+  // byte beside the route
+  const Gate cur = current_gate();
   GemmArgs gf;
   EpiArgs e;
   hipError_t err = nvfp4_gemm_prepare(a_q4, a_s4, a_ts4, w_q, w_s, w_ts, M, N, K, o, ws, ws_bytes,
-                                      Gate{route, kRouteNvfp4}, st, gf, e);
+                                      Gate{route, kRouteNvfp4, 0u, cur.flags, cur.bits}, st,
+                                      gf, e);
   if (err != hipSuccess) return err;
   const bool split = ws_bytes >= int8_i8_gemm_ws_bytes(M, N, K) &&
                      int8_i8_gemm_ws_bytes(M, N, K) > 0;
   I8Args gi = i8_args(a_q8, a_s8, w8, w_ts, M, N, K, ws, split);
-  gi.gate = Gate{route, kRouteInt8, kRouteNvfp4};     // a byte with both bits: NVFP4 only
-  // the whole tiles: the kernel reads the route itself
+  // a byte with both bits: NVFP4 only
+  gi.gate = Gate{route, kRouteInt8, kRouteNvfp4, cur.flags, cur.bits};
+  // the whole tiles: the kernel reads the route itself, its bodies check
+  // the thread's gate
   GemmArgs gfm = gf;
   I8Args gim = gi;
-  gfm.gate = Gate{nullptr, 0u};
-  gim.gate = Gate{nullptr, 0u};
+  gfm.gate = cur;
+  gim.gate = cur;
   if (!gfm.main_tiles) gfm.grid_main = 0;
   if (!gim.main_tiles) gim.grid_main = 0;
   const int grid = gfm.grid_main > gim.grid_main ? gfm.grid_main : gim.grid_main;

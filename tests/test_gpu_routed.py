@@ -193,3 +193,45 @@ def test_qlinear_routed(M, N, K, bias, gelu, amax, route):
         assert int(slots.max()) == int(ref_slots.max())
         yb = host(y.view(t.int16)).astype(np.uint32) & 0x7FFF
         assert int(slots.max()) == int(yb.max()) << 16
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 192), (600, 704, 3840), (4452, 1960, 1920)])
+def test_qlinear_routed_under_thread_gate(M, N, K):
+    # a gate set with qa_set_gate applies to qlinear_routed as to every call:
+    # closed, no launch of either format touches y, the |max| words or the
+    # workspace's effect (one routed launch; a K split; the persistent INT8
+    # kernel); open, the outputs are those of the ungated call
+    qa, t = _qa(), torch()
+    x = dev(synth.activations(17, M, K, "normal"))
+    w = dev(synth.weight(17, 0, N, K))
+    a4 = qa.empty_nvfp4(M, K)
+    qa.act_quant(qa.NVFP4, x, a4[0], a4[1], a4[2], 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, M, K)))
+    a8 = qa.empty_int8_act(M, K)
+    qa.act_quant(qa.INT8, x, a8[0], a8[1])
+    wq = qa.empty_nvfp4(N, K)
+    qa.act_quant(qa.NVFP4, w, wq[0], wq[1], wq[2], 0,
+                 qa.workspace(qa.act_quant_workspace(qa.NVFP4, N, K)))
+    w8 = qa.empty_int8_planes(N, K)
+    assert qa.int8_weight_planes(wq[0], wq[1], w8, N, K) == 0
+    ws = qa.workspace(qa.qlinear_routed_workspace(M, N, K))
+    flag = t.zeros(1, dtype=t.uint8, device="cuda")
+    for route in (qa.ROUTE_NVFP4, qa.ROUTE_INT8):
+        ref = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+        ref_slots = t.zeros(1024, dtype=t.int32, device="cuda")
+        qa.qlinear_routed(_byte(route), a4[0], a4[1], a4[2], a8[0], a8[1], wq[0], wq[1], wq[2],
+                          w8, ref, M, N, K, epi=qa.EPI_GELU_TANH, y_amax=ref_slots, ws=ws)
+        for state in (0, 4, 3):                   # closed, closed (other bit), open
+            flag.fill_(state)
+            y = t.full((M, N), -3.0, dtype=t.bfloat16, device="cuda")
+            slots = t.zeros(1024, dtype=t.int32, device="cuda")
+            with qa.gate(flag, 3):
+                qa.qlinear_routed(_byte(route), a4[0], a4[1], a4[2], a8[0], a8[1], wq[0], wq[1],
+                                  wq[2], w8, y, M, N, K, epi=qa.EPI_GELU_TANH, y_amax=slots, ws=ws)
+            t.cuda.synchronize()
+            if state & 3:
+                assert t.equal(y.view(t.int16), ref.view(t.int16)), (route, state)
+                assert int(slots.max()) == int(ref_slots.max())
+            else:
+                assert bool((y == -3.0).all()), (route, state)
+                assert int(slots.abs().max()) == 0
