@@ -78,8 +78,8 @@ nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t 
 // one float32 tensor scale).  K % 16 == 0, so a group is the even vector v and v + 1, held
 // by lanes 2j and 2j+1.  Outputs are indexed by v alone: code word v of
 // the [M][K/2] code array and scale byte v / 2 of the [M][K/16] scales.
-// (run by workgroup `bid` of `nblk`)
-template <int U>
+// (run by workgroup `bid` of `nblk`; CONTIG: ldx == K, one flat index)
+template <int U, bool CONTIG>
 __device__ __forceinline__ void nvfp4_encode_body(const uint16_t* __restrict__ x, int64_t M,
                                                   int64_t K, int64_t ldx, uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ scales,
@@ -88,7 +88,6 @@ __device__ __forceinline__ void nvfp4_encode_body(const uint16_t* __restrict__ x
                                                   int given, int bid, int nblk) {
   const int64_t vpr = K / 8;                               // vectors per row
   const int64_t nvec = M * vpr;
-  const bool contig = ldx == K;
   const bool small = nvec <= 0xFFFFFFFFll;
   const int64_t sweep = (int64_t)nblk * 256 * U;
   const int64_t start = (int64_t)bid * 256 * U + threadIdx.x;
@@ -97,7 +96,7 @@ __device__ __forceinline__ void nvfp4_encode_body(const uint16_t* __restrict__ x
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + u * 256;
       int64_t off = v * 8;
-      if (!contig) {
+      if constexpr (!CONTIG) {
         const int64_t row = small ? (int64_t)((uint32_t)v / (uint32_t)vpr) : v / vpr;
         off = row * ldx + (v - row * vpr) * 8;
       }
@@ -152,15 +151,15 @@ __device__ __forceinline__ void nvfp4_encode_body(const uint16_t* __restrict__ x
   }
 }
 
-template <int U>
+template <int U, bool CONTIG>
 __global__ void __launch_bounds__(256)
 nvfp4_encode_vec_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
                         uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
                         float* __restrict__ tscale, const float* __restrict__ partial,
                         int nparts, int given, Gate gate) {
   if (gated_off(gate)) return;
-  nvfp4_encode_body<U>(x, M, K, ldx, q, scales, tscale, partial, nparts, given, (int)blockIdx.x,
-                       (int)gridDim.x);
+  nvfp4_encode_body<U, CONTIG>(x, M, K, ldx, q, scales, tscale, partial, nparts, given,
+                               (int)blockIdx.x, (int)gridDim.x);
 }
 
 // ----------------------------------------------------------------- INT8 --
@@ -243,9 +242,14 @@ act_quant_routed_kernel(const uint8_t* __restrict__ route, const uint16_t* __res
   if (gated_off(gate)) return;
   const uint32_t r = *route;
   if (r & kRouteNvfp4) {
-    if ((int)blockIdx.x < nvfp4_blocks)
-      nvfp4_encode_body<U>(x, M, K, ldx, q4, s4, ts4, partial, nparts, given, (int)blockIdx.x,
-                           nvfp4_blocks);
+    if ((int)blockIdx.x < nvfp4_blocks) {
+      if (ldx == K)
+        nvfp4_encode_body<U, true>(x, M, K, ldx, q4, s4, ts4, partial, nparts, given,
+                                   (int)blockIdx.x, nvfp4_blocks);
+      else
+        nvfp4_encode_body<U, false>(x, M, K, ldx, q4, s4, ts4, partial, nparts, given,
+                                    (int)blockIdx.x, nvfp4_blocks);
+    }
   } else if (r & kRouteInt8) {
     for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M;
          row += (int64_t)gridDim.x * 4)
@@ -289,8 +293,13 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t M, int64_t K, int64_t l
   int64_t eblk = (M * (K / 8) + 256 * kEncU - 1) / (256 * kEncU);
   if (eblk > kEncBlocks) eblk = kEncBlocks;
   if (eblk < 1) eblk = 1;
-  hipLaunchKernelGGL(nvfp4_encode_vec_kernel<kEncU>, dim3((unsigned)eblk), dim3(256), 0, stream,
-                     x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0, gt);
+  if (ldx == K)
+    hipLaunchKernelGGL((nvfp4_encode_vec_kernel<kEncU, true>), dim3((unsigned)eblk), dim3(256), 0,
+                       stream, x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0, gt);
+  else
+    hipLaunchKernelGGL((nvfp4_encode_vec_kernel<kEncU, false>), dim3((unsigned)eblk), dim3(256),
+                       0, stream, x, M, K, ldx, q, scales, tscale, partial, nblk, given ? 1 : 0,
+                       gt);
   return hipGetLastError();
 }
 

@@ -42,19 +42,24 @@ __device__ __forceinline__ float recip0(float y) { return y == 0.0f ? 0.0f : 1.0
 //   normal range (s >= 2^-6): round the float32 encoding to 3 mantissa
 //   bits (a carry moves into the exponent), then rebias 127 -> 7;
 //   below 2^-6 the E4M3 step is 2^-9: code = rint(s * 512), up to 8 = 0x08.
+// Both ranges are computed and one is selected (no branch: lanes of a
+// wave take different ranges).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (s < 0.015625f) return (uint32_t)rintf(s * 512.0f);
-  uint32_t u = __float_as_uint(s);
+  const uint32_t sub = (uint32_t)rintf(s * 512.0f);
+  const uint32_t u = __float_as_uint(s);
   uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;   // exp8:mant3
-  r -= (127u - 7u) << 3;
-  return r > 0x7Eu ? 0x7Eu : r;
+  r -= (127u - 7u) << 3;                                   // (wraps below 2^-6: not selected)
+  r = r > 0x7Eu ? 0x7Eu : r;
+  return s < 0.015625f ? sub : r;
 }
 
-// Value of a non-negative E4M3FN code 0..0x7E.
+// Value of a non-negative E4M3FN code 0..0x7E (both forms computed, one
+// selected).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = c >> 3, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;               // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t e = c >> 3, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;                  // m * 2^-9
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 // E2M1 codes of two float32 values, packed into byte `sel` of `old` (the
