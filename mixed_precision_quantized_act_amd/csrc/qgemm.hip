@@ -76,12 +76,14 @@ static size_t r256(size_t v) { return (v + 255) / 256 * 256; }
 // that workspace sizes are too; on a device with another CU count the plan
 // is only less well fitted.  Every slice stores its fp32 partial sums in the workspace;
 // a second launch adds them per tail tile and runs the epilogue (no
-// workgroup waits for another inside a launch).
-// (the split is worth it only if the round gets shorter by more than the
-// slice and fixup launches cost: measured, the fixup alone takes about as
-// long as 15-20 raw units of a tile -- the QKV shape, 30 units in 3
-// slices, ran 5 % slower split; the 7680-wide down projection, 120 units
-// in 4, 10 % faster)
+// workgroup waits for another inside a launch), four workgroups per tail
+// tile so that the fixup's loads spread over more CUs and fewer sequential
+// batches (74 tail tiles of the QKV shape: 22.7 us with one workgroup per
+// tile).  (The split is worth it only if the round gets shorter by more
+// than the slice and fixup launches cost: at 8 units the QKV and FFN-up
+// shapes, 30 units in 3-4 slices, measured no faster, the 1920-wide O
+// projection 2 % faster; the 7680-wide down projection, 120 units in 4,
+// is 10 % faster.)
 static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   const int total = (int)(((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN));
   return plan_split(total, (int)units_of(K), kCUs, kMaxSplits, kSplitMinSaved);
@@ -182,7 +184,7 @@ static void launch_one(int parts, const GemmArgs& g, const EpiArgs& e, hipStream
   if (!tail || !(parts & kPartsTails)) return;
   launch_mode<I8, kEpiPlain, kSlice>(tail * g.splits, ev && !g.main_tiles ? g_ev_before : nullptr,
                                      nullptr, g, e, st);
-  launch_mode<I8, kEpi, kFixup>(tail, nullptr, ev ? g_ev_after : nullptr, g, e, st);
+  launch_mode<I8, kEpi, kFixup>(4 * tail, nullptr, ev ? g_ev_after : nullptr, g, e, st);
 }
 
 static hipError_t launch_gemm(bool i8, const GemmArgs& g, const EpiArgs& e, hipStream_t st,

@@ -169,9 +169,10 @@ struct RawWords<true> {
 
 // Launch modes: kWhole -- whole tiles (all of them, or all but the tail
 // tiles of a K-split call); kSlice -- one K slice of a tail tile per
-// workgroup, storing its fp32 partial sums; kFixup -- one workgroup per tail
-// tile, adding the slices' partial sums (in slice order) and running the
-// epilogue.  Each is its own kernel so that the whole-tile kernel carries
+// workgroup, storing its fp32 partial sums; kFixup -- four workgroups per
+// tail tile, one per quadrant (the slices' partial sums of one wave of the
+// slice workgroups), each of whose waves adds one row of MFMA tiles' sums
+// (in slice order) and runs the epilogue on those 32 x 128 outputs.  Each is its own kernel so that the whole-tile kernel carries
 // none of the slice bookkeeping (modes kWhole, kSlice, kFixup).
 
 // The kernel body: workgroup `bid` of a launch in mode kMode, with the
@@ -188,8 +189,13 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
   // tile-rows at a time so that concurrent tiles share A rows and B rows.
   // A kSlice workgroup computes slice `slice` of tail tile main_tiles +
   // bid / splits: raw units u_begin .. u_begin + u_count - 1.
+  // a fixup launch has four workgroups per tail tile, one per quadrant
+  // (the partial sums of the slices' wave fq), each wave adding one row
+  // of 32 x 128 outputs
+  const int fq = bid & 3;
   TileWork tw;
-  if (!tile_work(kMode, bid, g.main_tiles, g.splits, g.split_units, g.units, tw))
+  if (!tile_work(kMode, kMode == kFixup ? (bid >> 2) : bid, g.main_tiles, g.splits,
+                 g.split_units, g.units, tw))
     return;
   const int logical = tw.logical, slice = tw.slice, u_begin = tw.u_begin, u_count = tw.u_count;
   int tm, tn;
@@ -198,7 +204,8 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = kMode == kFixup ? (fq >> 1) : (wave >> 1);
+  const int wn = kMode == kFixup ? (fq & 1) : (wave & 1);
   const int64_t K = g.K;
 
   // Buffer resources based at this tile's first row; rows past the operand
@@ -482,11 +489,11 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
     // the tile's sum over its K slices, added in slice order
     const f32x4* const base = reinterpret_cast<const f32x4*>(g.part) +
                               (size_t)(logical - g.main_tiles) * g.splits * (kPartTile / 4) +
-                              wave * 4096 + lane;
+                              fq * 4096 + lane;
     const int ns = g.splits;
     constexpr int kPair = 2;              // MFMA tiles whose chunks load together
-#pragma unroll
-    for (int i = 0; i < kFM; ++i)
+    {
+      const int i = wave;                 // this wave's row of MFMA tiles
 #pragma unroll
       for (int j0 = 0; j0 < kFN; j0 += kPair) {
         // the 4 chunks of MFMA tiles (i, j0 .. j0 + kPair - 1) from every
@@ -517,19 +524,27 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
           // operands (it adds +0, which changes no sum: none is -0), so
           // that the 256 sums do not crowd the ordinary registers
           const f16x8 z = {};
-          acc[i][j0 + jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, tot, 0, 0, 0);
+          acc[0][j0 + jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, tot, 0, 0, 0);
         }
         // bound the loads in flight to kPair MFMA tiles' chunks
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
   }
   if constexpr (kMode != kSlice) {
 
   // ---- epilogue (store_tile): the tensor scales, and for INT8 the row
   // scales of the lane's rows (rows past M read row M-1; never stored)
+  const int c = lane & 31;
+  if constexpr (kMode == kFixup) {
+    const int64_t wave_row0 = m0 + wm * 128 + 32 * wave;
+    const int64_t wave_col0 = n0 + wn * 128;
+    float rs[1];
+    rs[0] = I8 ? g.a_rs[min<int64_t>(wave_row0 + c, e.M - 1)] * alpha : alpha;
+    store_tile<kEpi, 1>(acc, rs, wave_row0, wave_col0, smem + wave * 8192 * kPassTiles, e, lane);
+  } else {
   const int64_t wave_row0 = m0 + wm * 128;
   const int64_t wave_col0 = n0 + wn * 128;
-  const int c = lane & 31;
   float rs[kFM];
 #pragma unroll
   for (int i = 0; i < kFM; ++i) {
@@ -538,6 +553,7 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
     rs[i] = I8 ? row_scale[i] * alpha : alpha;
   }
   store_tile<kEpi, kFM>(acc, rs, wave_row0, wave_col0, smem + wave * 8192 * kPassTiles, e, lane);
+  }
   }
 }
 

@@ -36,7 +36,9 @@ QACT_HD inline SplitPlan plan_split(int total, int units, int cus, int max_split
 }
 
 // Launch modes: whole tiles (grid 8 ceil(main_tiles / 8)), the K slices of
-// the tail tiles (grid tail * splits) and their fixup (grid tail).
+// the tail tiles (grid tail * splits) and their fixup (workgroup bid: tail
+// tile bid; the fp16 kernel launches four workgroups per tail tile and
+// passes bid / 4).
 enum { kWhole = 0, kSlice = 1, kFixup = 2 };
 
 // Workgroup bid of a launch in `mode`: its logical tile and the units it
