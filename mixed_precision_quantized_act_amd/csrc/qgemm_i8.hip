@@ -341,8 +341,12 @@ __device__ __forceinline__ void i8_tile_body(const I8Args& g, const EpiArgs& e, 
 
   // tile of this workgroup: XCD-aware order as in the fp16 kernel (each
   // XCD a contiguous range of logical tiles, grouped 8 tile-rows at a time)
+  // a fixup launch has two workgroups per tail tile (half fh of its rows)
+  const int fh = bid & 1;
   TileWork tw;
-  if (!tile_work(kMode, bid, g.main_tiles, g.splits, g.split_units, g.units, tw)) return;
+  if (!tile_work(kMode, kMode == kFixup ? (bid >> 1) : bid, g.main_tiles, g.splits,
+                 g.split_units, g.units, tw))
+    return;
   const int logical = tw.logical, slice = tw.slice, u_begin = tw.u_begin, u_count = tw.u_count;
   int tm, tn;
   tile_coords(logical, g.mt, g.nt, 8, tm, tn);
@@ -464,44 +468,58 @@ __device__ __forceinline__ void i8_tile_body(const I8Args& g, const EpiArgs& e, 
       return;
     }
   } else {
-    // the tile's sums over its K slices (integer sums: exact in any order)
+    // the tile's sums over its K slices (integer sums: exact in any order).
+    // Workgroup half fh takes the slice waves fq = 2 fh, 2 fh + 1; its wave
+    // w adds row tile w & 1 of slice wave 2 fh + (w >> 1): all 8 plane
+    // tiles of one 32-row block, into acc[0][*]
+    const int fq = 2 * fh + (wave >> 1), i = wave & 1;
     const i32x4* const base = reinterpret_cast<const i32x4*>(g.part) +
                               (size_t)(logical - g.main_tiles) * g.splits * (kPartTile / 4) +
-                              wave * 4096 + lane;
+                              fq * 4096 + lane;
     const int ns = g.splits;
+    constexpr int kPair = 2;              // plane tiles whose chunks load together
 #pragma unroll
-    for (int i = 0; i < kFM; ++i)
+    for (int j0 = 0; j0 < kFN; j0 += kPair) {
+      i32x4 v[kPair][4][kMaxSplits];
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) {
-        i32x4 v[4][kMaxSplits];
+      for (int jj = 0; jj < kPair; ++jj)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
           for (int sl = 0; sl < kMaxSplits; ++sl)
-            v[r4][sl] = sl < ns ? base[(size_t)sl * (kPartTile / 4) + ((i * kFN + j) * 4 + r4) * 64]
-                                : i32x4{0, 0, 0, 0};
+            v[jj][r4][sl] =
+                sl < ns ? base[(size_t)sl * (kPartTile / 4) + ((i * kFN + j0 + jj) * 4 + r4) * 64]
+                        : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < kPair; ++jj) {
         i32x16 tot;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          i32x4 sum = v[r4][0];
+          i32x4 sum = v[jj][r4][0];
 #pragma unroll
-          for (int sl = 1; sl < kMaxSplits; ++sl) sum += v[r4][sl];
+          for (int sl = 1; sl < kMaxSplits; ++sl) sum += v[jj][r4][sl];
 #pragma unroll
           for (int t = 0; t < 4; ++t) tot[4 * r4 + t] = sum[t];
         }
         // into the accumulation registers through an MFMA with zero operands
         const i32x4 z = {0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(z, z, tot, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        acc[0][j0 + jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(z, z, tot, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if constexpr (kMode != kSlice) {
+    // a fixup wave owns one 32-row block of the tile, b0 (row tile 0 of
+    // acc); the others their 64 rows
+    constexpr int FM = kMode == kFixup ? 1 : kFM;
+    const int b0 = kMode == kFixup ? 2 * (2 * fh + (wave >> 1)) + (wave & 1) : 0;
+    const int64_t row0 = kMode == kFixup ? m0 + 32 * b0 : wave_row0;
     if constexpr (kEpi == kEpiAcc) {
       // H (hi plane, tiles j >= 4) and L (lo plane) as they are
 #pragma unroll
-      for (int i = 0; i < kFM; ++i) {
-        const int64_t row = wave_row0 + 32 * i + lr;
+      for (int i = 0; i < FM; ++i) {
+        const int64_t row = row0 + 32 * i + lr;
 #pragma unroll
         for (int j = 0; j < kFN / 2; ++j)
 #pragma unroll
@@ -517,9 +535,10 @@ __device__ __forceinline__ void i8_tile_body(const I8Args& g, const EpiArgs& e, 
       // rows holds s_a s_Tw (multiplied once per row as it was staged)
       // i8_epilogue's arithmetic, written out: called here, the register
       // allocation of this kernel spills 12-37 registers
-      float rs[kFM];
+      float rs[FM];
 #pragma unroll
-      for (int i = 0; i < kFM; ++i) rs[i] = rows[64 * wave + 32 * i + lr];
+      for (int i = 0; i < FM; ++i)
+        rs[i] = rows[(kMode == kFixup ? 32 * b0 : 64 * wave) + 32 * i + lr];
       f32x4 cf[kFN / 2][4];
 #pragma unroll
       for (int j = 0; j < kFN / 2; ++j)
@@ -530,7 +549,7 @@ __device__ __forceinline__ void i8_tile_body(const I8Args& g, const EpiArgs& e, 
         return __builtin_fmaf((float)acc[i][j + kFN / 2][r], 256.0f, (float)acc[i][j][r]) *
                cf[j][r >> 2][r & 3];
       };
-      store_tile<kEpi, kFM>(val, rs, wave_row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
+      store_tile<kEpi, FM>(val, rs, row0, n0, smem + wave * 8192 * kPassTiles, e, lane);
     }
   }
 }
@@ -774,7 +793,7 @@ void launch_one(const I8Args& g, const EpiArgs& e, hipStream_t st) {
   if (!tail) return;
   launch_mode<kEpiPlain, kSlice>(tail * g.splits, g.main_tiles ? nullptr : g_ev_before, nullptr,
                                  g, e, st);
-  launch_mode<kEpi, kFixup>(tail, nullptr, g_ev_after, g, e, st);
+  launch_mode<kEpi, kFixup>(2 * tail, nullptr, g_ev_after, g, e, st);
 }
 
 }  // namespace
@@ -907,7 +926,7 @@ hipError_t launch_routed_gemm(const uint8_t* route, const uint8_t* a_q4, const u
     const int tail = gi.mt * gi.nt - gi.main_tiles;
     if (tail) {
       launch_mode<kEpiPlain, kSlice>(tail * gi.splits, nullptr, nullptr, gi, e, st);
-      launch_mode<kEpi, kFixup>(tail, nullptr, nullptr, gi, e, st);
+      launch_mode<kEpi, kFixup>(2 * tail, nullptr, nullptr, gi, e, st);
     }
   };
   switch (kind) {
