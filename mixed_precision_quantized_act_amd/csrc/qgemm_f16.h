@@ -294,25 +294,33 @@ __device__ __forceinline__ void qgemm_body(const GemmArgs& g, const EpiArgs& e, 
     u32x2 b[kFN];
     uint32_t bs[kFN];
   };
+  // each stage's reads address from one lane base per region (A codes, A
+  // scale words, W codes, W scale words): the tiles' offsets are constants
+  // that the LDS reads take as immediates
+  const uint32_t la = (uint32_t)a_base * (I8 ? 64u : 32u), lb = (uint32_t)b_base * 32u;
+  const uint32_t las = (uint32_t)a_base * 4u, lbs = (uint32_t)b_base * 4u;
   auto read_raw = [&](int t, RawS& r) {
     const uint8_t* s = smem + ((t >> 1) % kRawSlots) * R::kSlot;
     const int sh = t & 1;
+    const uint8_t* const pa =
+        s + la + (I8 ? 16u * (uint32_t)((2 * sh + lh) ^ i8_sw) : (uint32_t)((16 * sh) ^ nv_off));
+    const uint8_t* const pb = s + lb + (uint32_t)((16 * sh) ^ nv_off);
+    const uint8_t* const pas = s + las;
+    const uint8_t* const pbs = s + lbs;
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
-      const int row = a_base + 32 * i;
       if constexpr (I8) {
-        r.a[i] = *reinterpret_cast<const AW*>(s + R::kA + row * 64 + 16 * ((2 * sh + lh) ^ i8_sw));
+        r.a[i] = *reinterpret_cast<const AW*>(pa + R::kA + 32 * 64 * i);
         r.as[i] = 0u;
       } else {
-        r.a[i] = *reinterpret_cast<const AW*>(s + R::kA + row * 32 + ((16 * sh) ^ nv_off));
-        r.as[i] = *reinterpret_cast<const uint32_t*>(s + R::kAS + row * 4);
+        r.a[i] = *reinterpret_cast<const AW*>(pa + R::kA + 32 * 32 * i);
+        r.as[i] = *reinterpret_cast<const uint32_t*>(pas + R::kAS + 32 * 4 * i);
       }
     }
 #pragma unroll
     for (int j = 0; j < kFN; ++j) {
-      const int n = b_base + 32 * j;
-      r.b[j] = *reinterpret_cast<const u32x2*>(s + R::kB + n * 32 + ((16 * sh) ^ nv_off));
-      r.bs[j] = *reinterpret_cast<const uint32_t*>(s + R::kBS + n * 4);
+      r.b[j] = *reinterpret_cast<const u32x2*>(pb + R::kB + 32 * 32 * j);
+      r.bs[j] = *reinterpret_cast<const uint32_t*>(pbs + R::kBS + 32 * 4 * j);
     }
   };
   // fp16 fragments of a stage: (a0, b0) for k-step 0, (a1, b1) for k-step 1
