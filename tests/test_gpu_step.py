@@ -69,11 +69,13 @@ def test_gate_closed_leaves_outputs():
 class _Stack:
     """Weights, buffers and both drivers of the small stack."""
 
-    def __init__(self):
+    def __init__(self, L=L, H=H, F=F, M=M, seed=31):
         qa, t = _qa(), torch()
         self.qa, self.t = qa, t
+        self.L, self.J, self.H, self.F, self.M = L, J, H, F, M
+        SHAPES = [(3 * H, H), (H, H), (F, H), (H, F)]
         gen = t.Generator(device="cuda")
-        gen.manual_seed(31)
+        gen.manual_seed(seed)
         qw = qa.workspace(qa.act_quant_workspace(qa.NVFP4, F, F))
         self.layers = []
         for _ in range(L):
@@ -122,6 +124,7 @@ class _Stack:
             b.zero_()
 
     def linear(self, fmt, x, ldx, lay, y, gelu):
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa, t = self.qa, self.t
         q, sc, ts, N, K, w8 = lay
         xv = t.as_strided(x, (M, K), (ldx, 1)).view(t.int16)
@@ -137,6 +140,7 @@ class _Stack:
             qa.qlinear_int8(aq, self.a8[1], q, sc, ts, y, M, N, K, epi=epi, ws=self.gws, w8=w8)
 
     def gemm(self, fmt, lay, y, gelu, K):
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa = self.qa
         q, sc, ts, N, _, w8 = lay
         epi = qa.EPI_GELU_TANH if gelu else qa.EPI_NONE
@@ -151,6 +155,7 @@ class _Stack:
     def routed_linear(self, flag, x, ldx, lay, y, gelu):
         """One act_quant launch and one GEMM launch in the format the linear's
         flag selects."""
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa, t = self.qa, self.t
         K = lay[4]
         xv = t.as_strided(x, (M, K), (ldx, 1)).view(t.int16)
@@ -167,6 +172,7 @@ class _Stack:
         """The compute path of block l (linears in formats fmts, or both
         formats gated on the block's linear flags; routed: one act_quant
         launch for both)."""
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa, t = self.qa, self.t
         i16 = lambda b: b.view(t.int16)
         lay = self.layers[l]
@@ -193,6 +199,7 @@ class _Stack:
 
     def host_run(self, xs, tau, delta):
         """Host decisions, as the benchmark drives the stack."""
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa, t = self.qa, self.t
         i16 = lambda b: b.view(t.int16)
         self.reset()
@@ -235,6 +242,7 @@ class _Stack:
         """One step, every path enqueued under its gate (routed: the calls
         that take their format or ring slot from the gate byte, one launch
         each)."""
+        L, J, H, F, M = self.L, self.J, self.H, self.F, self.M
         qa, t = self.qa, self.t
         i16 = lambda b: b.view(t.int16)
         qa.decide_step(self.sums, self.alpha_d, self.beta_d, tau, delta, L, J, self.t_ctr,
@@ -262,10 +270,10 @@ class _Stack:
             cur = out
 
 
-def _inputs():
+def _inputs(M=M, H=H, steps=10):
     x = synth.activations(1, M, H, "normal")
     xs = []
-    for step in range(10):
+    for step in range(steps):
         x = synth.drift(1, step, x)
         xs.append(dev(x).view(torch().bfloat16))
     return xs
@@ -315,6 +323,39 @@ def test_device_decisions_eager_and_graph(delta, routed):
         np.testing.assert_array_equal(host(st.mask_out), ref[step][0], err_msg=f"graph mask, step {step}")
         np.testing.assert_array_equal(host(st.skip_out), ref[step][1], err_msg=f"graph skip, step {step}")
         np.testing.assert_array_equal(host(st.outs[-1]), ref[step][2], err_msg=f"graph output, step {step}")
+
+
+def test_device_decisions_full_width_graph():
+    # the same at the CogVideoX-2B block width (17776 tokens, H 1920, FFN
+    # 7680): two blocks over five steps, routed calls captured once and
+    # replayed, against host decisions bit for bit; the routed GEMM takes
+    # its persistent-INT8 path (QKV, up), its one-launch path and K splits
+    # (down), the NVFP4 scale re-layout; delta 10 skips blocks from t = 2
+    t = torch()
+    st = _Stack(L=2, H=1920, F=7680, M=17776, seed=7)
+    xs = _inputs(17776, 1920, 5)
+    ref, tau = st.host_run(xs, None, 10.0)
+    skips = np.array([r[1] for r in ref])
+    assert skips[2:].any() and not skips[:2].any()
+    masks = np.array([r[0] for r in ref[1:]])
+    assert 0 < masks.sum() < masks.size                 # both formats occur
+    st.reset()
+    g = t.cuda.CUDAGraph()
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            st.device_step(tau, 10.0, routed=True)
+    t.cuda.current_stream().wait_stream(s)
+    st.reset()
+    t.cuda.synchronize()
+    for step, xd in enumerate(xs):
+        st.x_in.copy_(xd)
+        g.replay()
+        t.cuda.synchronize()
+        np.testing.assert_array_equal(host(st.mask_out), ref[step][0], err_msg=f"mask, step {step}")
+        np.testing.assert_array_equal(host(st.skip_out), ref[step][1], err_msg=f"skip, step {step}")
+        assert np.array_equal(host(st.outs[-1]), ref[step][2]), f"output, step {step}"
 
 
 def test_decide_step_against_oracle_rules():
